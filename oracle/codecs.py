@@ -36,12 +36,14 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """float32 -> bfloat16 bits, round to nearest, ties to even.
+    """float32 -> bfloat16 bits, round to nearest, ties to even (IEEE 754).
 
     For each finite value the two bfloat16 neighbours are the value with its
     low 16 bits cleared (towards zero) and the next one away from zero; the
     nearer wins, measured exactly in float64, and a tie picks the neighbour
-    whose last kept bit is 0.  NaN maps to a quiet NaN with the same sign.
+    whose last kept bit is 0.  Above the largest finite bfloat16 the next
+    neighbour is infinity, weighed as 2**128.  NaN maps to a quiet NaN with
+    the same sign.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
@@ -51,6 +53,11 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     lo_v = lo.view(np.float32).astype(np.float64)
     with np.errstate(over="ignore", invalid="ignore"):
         hi_v = hi.view(np.float32).astype(np.float64)
+        # Past the largest finite bfloat16 the upper neighbour is infinity;
+        # IEEE rounding measures against 2**128 (the next power of the
+        # exponent range), so values beyond the midpoint overflow to inf.
+        over = np.isinf(hi_v) & np.isfinite(xv)
+        hi_v = np.where(over, np.copysign(2.0 ** 128, xv), hi_v)
         d_lo = np.abs(xv - lo_v)
         d_hi = np.abs(hi_v - xv)
     lo_even = ((lo >> np.uint32(16)) & np.uint32(1)) == 0

@@ -95,7 +95,11 @@ def test_bf16_matches_torch_rne():
     x = np.concatenate([
         rng.standard_normal(300000).astype(np.float32),
         (rng.standard_normal(10000) * 1e-39).astype(np.float32),  # subnormals
-        np.array([3.3895314e38, -3.3895314e38, 1.0, -0.0, 0.0], np.float32),
+        np.array([3.3895314e38, -3.3895314e38, 1.0, -0.0, 0.0, np.inf, -np.inf], np.float32),
+        # around the overflow threshold: largest finite float32, the bf16
+        # midpoint 0x7F7F8000 (ties up to inf) and its neighbours
+        np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0xFF7F8000, 0x7F7F0001],
+                 np.uint32).view(np.float32),
     ])
     # exact ties: bf16 value + half an ulp
     base = rng.integers(0, 0x7F00, 20000, dtype=np.uint32) << np.uint32(16)
