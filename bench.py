@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-KV decode step on one MI355X.
+
+A step is one ``decode_step`` call (RoPE, append, paged attention over the
+whole ragged batch, split merge) for one layer of the workload.  Inputs are
+synthetic, drawn on the device, and resident in HBM before timing starts.
+Consecutive steps cycle over enough independent pools ("layers") that each
+step reads a cold working set of at least 1 GB, larger than the 256 MB
+Infinity Cache.
+
+Prints one JSON line: the metric is the algorithmic HBM bandwidth of the
+step (bytes the method must move / step time) with its fraction of the
+8 TB/s peak and the decode tokens/s per layer; ``roofline`` reports the
+attention kernel's own duration from HIP events on its launch stream;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "paged decode attention: HBM GB/s (% of peak) and decode tokens/s per layer"
+ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the step must move: cached K/V read once per KV head, the new
+    K/V written, q/k_new/v_new read, out written, the block-table entries,
+    positions and lengths, the RoPE rows and (fp8) the scales."""
+    c = wl.cfg
+    s_kv, s_io = ELEM[c.kv_dtype], ELEM[c.io_dtype]
+    L = wl.context_lens.astype(np.int64)
+    per_tok = 2 * c.n_kv_heads * c.head_dim * s_kv
+    total = int(((L - 1) * per_tok).sum())                       # read cached K, V
+    total += wl.batch * per_tok                                  # write new K, V
+    total += wl.batch * (2 * c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * s_io
+    total += int((4 * ((L + c.block_size - 1) // c.block_size) + 8).sum())
+    total += wl.batch * c.head_dim * 4                           # cos + sin rows
+    if c.kv_dtype == "fp8":
+        total += 16 * c.n_kv_heads
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "plan.h", "kernels.h"):
+        with open(os.path.join(ROOT, "paged_kv_decode_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, per_launch_alg: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def synth_pool_chunks(wl, device, chunk_blocks: int = 4096):
+    """Cached K/V drawn on the device (float32 N(0,1), seeded per chunk) and
+    cast to the cache type with torch's conversions: bf16 round-to-nearest,
+    fp8 with per-head scales amax/448 and saturation.  Returns a generator of
+    (first_block, k_codes, v_codes) in the logical layout, and the scales."""
+    import torch
+    import workloads
+
+    c = wl.cfg
+    nb = wl.num_blocks
+    scales = None
+    if c.kv_dtype == "fp8":
+        amax = {"k_cache": torch.zeros(c.n_kv_heads, device=device),
+                "v_cache": torch.zeros(c.n_kv_heads, device=device)}
+        for b0 in range(0, nb, chunk_blocks):
+            n = min(chunk_blocks, nb - b0)
+            for w in amax:
+                x = workloads.device_normals(wl, w, device, b0, n)
+                amax[w] = torch.maximum(amax[w], x.abs().amax(dim=(0, 2, 3)))
+                del x
+        scales = tuple((amax[w] / 448.0).float().cpu().numpy() for w in ("k_cache", "v_cache"))
+
+    def cast(x, i):
+        if c.kv_dtype == "bf16":
+            return x.to(torch.bfloat16).view(torch.int16)
+        if c.kv_dtype == "f32":
+            return x
+        inv = torch.from_numpy(np.float32(1.0) / scales[i]).to(device)
+        return (x * inv.view(1, -1, 1, 1)).clamp(-448.0, 448.0).to(
+            torch.float8_e4m3fn).view(torch.uint8)
+
+    def chunks():
+        for b0 in range(0, nb, chunk_blocks):
+            n = min(chunk_blocks, nb - b0)
+            yield (b0, cast(workloads.device_normals(wl, "k_cache", device, b0, n), 0),
+                   cast(workloads.device_normals(wl, "v_cache", device, b0, n), 1))
+
+    return chunks, scales
+
+
+def synth_io(wl, device):
+    """q, k_new, v_new: host-drawn N(0,1) cast to the I/O dtype by torch."""
+    import torch
+    import workloads
+
+    dt = torch.float32 if wl.cfg.io_dtype == "f32" else torch.bfloat16
+    host = {w: workloads.host_normals(wl, w) for w in ("q", "k_new", "v_new")}
+    return {w: torch.from_numpy(x).to(device).to(dt) for w, x in host.items()}
+
+
+def setup_layers(wl, n_layers, device):
+    """Pools filled with device-drawn values, plus the step's inputs."""
+    import torch
+    import paged_kv_decode_step_amd as pkv
+    from paged_kv_decode_step_amd import pool_io
+
+    c = wl.cfg
+    chunks, scales = synth_pool_chunks(wl, device)
+    pools = []
+    for _ in range(n_layers):
+        pool = pkv.KVPool(wl.num_blocks, c.block_size, c.n_kv_heads, c.head_dim, c.kv_dtype)
+        pool.set_rope(c.rope_theta, wl.max_position)
+        if scales is not None:
+            pool.set_fp8_scales(*scales)
+        pools.append(pool)
+    for b0, k, v in chunks():
+        for pool in pools:
+            pool_io.write_logical(pool, k, v, b0)
+        del k, v
+    tens = synth_io(wl, device)
+    tens["positions"] = torch.from_numpy(wl.positions.astype(np.int32)).to(device)
+    tens["block_tables"] = torch.from_numpy(wl.block_tables.astype(np.int32)).to(device)
+    tens["context_lens"] = torch.from_numpy(wl.context_lens.astype(np.int32)).to(device)
+    tens["out"] = torch.empty_like(tens["q"])
+    torch.cuda.synchronize()
+    return pools, tens, scales
+
+
+def cpu_baseline(wl, pool, tens, scales, budget_s: float):
+    """Time the CPU oracle on leading requests of the workload until about
+    `budget_s` seconds of work, reading their inputs back from the device."""
+    import torch
+    import oracle
+    from paged_kv_decode_step_amd import pool_io
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_problem as gp
+
+    def host_io(x):
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).cpu().numpy().view(np.uint16)
+        return x.cpu().numpy()
+    io = {w: host_io(tens[w]) for w in ("q", "k_new", "v_new")}
+
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ncores = len(os.sched_getaffinity(0))
+        limiter = threadpool_limits(ncores)
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's default
+        limiter, threads = None, len(os.sched_getaffinity(0))
+    c = wl.cfg
+    elapsed, done_bytes, done_req = 0.0, 0, 0
+    order = list(range(wl.batch))
+    for b in order:
+        nblk = int(wl.n_blocks_used()[b])
+        ids = torch.from_numpy(wl.block_tables[b, :nblk].astype(np.int64)).to(pool.k_storage().device)
+        k, v = pool_io.gather_blocks_logical(pool, ids)
+        kc, vc = gp.codes_from_torch(k, c.kv_dtype), gp.codes_from_torch(v, c.kv_dtype)
+        mwl, arrs = gp.mini_problem(wl, b, kc, vc, io, scales)
+        t0 = time.perf_counter()
+        oracle.decode_step(k_pool=arrs["k_pool"], v_pool=arrs["v_pool"], kv_dtype=c.kv_dtype,
+                           io_dtype=c.io_dtype, q=arrs["q"], k_new=arrs["k_new"],
+                           v_new=arrs["v_new"], positions=mwl.positions,
+                           block_tables=mwl.block_tables, context_lens=mwl.context_lens,
+                           block_size=c.block_size, rope_theta=c.rope_theta,
+                           k_scale=arrs["k_scale"], v_scale=arrs["v_scale"])
+        elapsed += time.perf_counter() - t0
+        done_bytes += algorithmic_bytes(mwl)
+        done_req += 1
+        if elapsed >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s",
+        "tokens_per_s_per_layer": round(done_req / elapsed, 2),
+        "cores": int(threads), "kind": "oracle",
+        "sample": f"first {done_req} of {wl.batch} requests of the same workload "
+                  f"({elapsed:.1f} s of numpy fp64 work; block gather, RoPE, append, "
+                  f"attention; input transfer excluded)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for the baseline (0 = skip)")
+    ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_decode_step_amd as pkv
+    import workloads
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = workloads.make_workload(args.config)
+    c = wl.cfg
+    alg = algorithmic_bytes(wl)
+    kv_bytes = int(((wl.context_lens.astype(np.int64)) * 2 * c.n_kv_heads * c.head_dim
+                    * ELEM[c.kv_dtype]).sum())
+    n_layers = max(1, math.ceil(args.min_cold_bytes / kv_bytes))
+    pools, t, scales = setup_layers(wl, n_layers, device)
+    print(f"# workload {c.name}: {wl.batch} requests, {alg/1e9:.3f} GB algorithmic per step, "
+          f"{n_layers} pool copies, {pools[0].info()['n_waves']} wavefronts", file=sys.stderr,
+          flush=True)
+
+    def step(i):
+        pkv.decode_step(pools[i % n_layers], t["q"], t["k_new"], t["v_new"], t["positions"],
+                        t["block_tables"], t["context_lens"], t["out"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, bracketed by synchronisation; events on the
+    # stream the kernels are launched on (torch's current stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # kernel durations from HIP events around each launch (a separate pass,
+    # so the events do not sit in the timed region above)
+    for p in pools:
+        p.enable_timing(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    attn_ms = merge_ms = 0.0
+    calls = 0
+    for p in pools:
+        a, m, n = p.read_timing()
+        attn_ms, merge_ms, calls = attn_ms + a, merge_ms + m, calls + n
+        p.enable_timing(False)
+    attn_avg = attn_ms / max(calls, 1)
+    merge_avg = merge_ms / max(calls, 1)
+
+    gbs = alg / (ms_per_step * 1e-3) / 1e9
+    achieved = alg / (attn_avg * 1e-3) / 1e9
+    traffic = measured_traffic(c.name, alg)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.kv_dtype if c.kv_dtype != "f32" else "f32",
+        "data": "synthetic",
+        "config": {"workload": c.name, "batch": wl.batch, "n_q_heads": c.n_q_heads,
+                   "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                   "block_size": c.block_size, "kv_dtype": c.kv_dtype,
+                   "io_dtype": c.io_dtype, "mean_context": float(wl.context_lens.mean()),
+                   "pool_copies": n_layers},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s_per_layer": round(wl.batch / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": alg,
+        "kernel_ms": {"attention": round(attn_avg, 5), "merge": round(merge_avg, 5)},
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, pools[0], t, scales, args.cpu_budget)
+    for p in pools:
+        p.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

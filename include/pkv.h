@@ -1,0 +1,240 @@
+/*
+ * pkv.h -- C ABI of the paged-KV decode step for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of an LLM server: every in-flight request of a ragged batch
+ * brings one new query token.  The step rotates the new query and key with
+ * RoPE, appends the new key/value into a pool of fixed-size KV blocks through
+ * the request's block table, and computes softmax(q K^T / sqrt(D)) V over the
+ * request's whole context, with query heads sharing KV heads (GQA) and a
+ * bf16, fp32 or FP8 (E4M3) cache.
+ *
+ * Where the operation is defined:
+ *   - fixed-size token blocks with per-request block tables, resolved inside
+ *     the attention kernel: "Scaling TensorRT-LLM: Kernel Fusion and Inflight
+ *     Batching in Production", section "The Paged KV-Cache: vLLM Borrowed by
+ *     TensorRT-LLM"; the scheduler, not the kernel, hands out blocks and
+ *     updates the tables (same page, "What the Scheduler Actually Does");
+ *   - RoPE applied inside the attention kernel and attention intermediates
+ *     kept on chip: same page, "What Gets Fused";
+ *   - KV-cache update fused with attention: "TensorRT-LLM" glossary
+ *     (inferensys.com), paragraph on the KV cache;
+ *   - KV heads shared by groups of query heads: "TensorRT-LLM Guide:
+ *     High-Throughput GPU Inference Engine", section "3. Custom Fused
+ *     Attention Kernels: FMHA and XQA";
+ *   - E4M3 cache with precomputed per-tensor scales: same page, section
+ *     "4. Native FP8 Quantization on NVIDIA Hopper & Blackwell" (here one
+ *     fp32 scale per KV head for K and one for V).
+ *
+ * Conventions.  All sizes are element counts unless named *_bytes.  Device
+ * pointers are HIP device addresses on the pool's device.  Every function
+ * returns a pkv_status and never throws; on failure pkv_last_error() returns a
+ * thread-local message.  Host-visible arguments are checked before any HIP
+ * call.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,      /* bad argument (null, out of range, mismatch) */
+  PKV_ERR_UNSUPPORTED = -2,  /* valid but not built (dtype/size combination) */
+  PKV_ERR_OOM = -3,          /* device allocation failed */
+  PKV_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_STATE = -5,        /* call order (e.g. no RoPE table set yet) */
+  PKV_ERR_DEVICE_DATA = -6   /* device-resident arguments out of range */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F32 = 0,               /* IEEE binary32 */
+  PKV_BF16 = 1,              /* bfloat16 */
+  PKV_FP8_E4M3 = 2           /* OCP E4M3FN: bias 7, max 448, no inf */
+} pkv_dtype;
+
+/* Opaque pool: owns the K and V block storage, the RoPE table, the FP8
+ * scales and the split-K workspace, all on one device (the current HIP
+ * device at kv_pool_create). */
+typedef struct pkv_pool pkv_pool;
+
+/* Physical layout of the pool, for callers that fill or inspect it.
+ *
+ * x = 16 / kv_elem_bytes (4 for fp32, 8 for bf16, 16 for fp8).
+ *   K element (block n, head h, slot t, dim d) lives at element offset
+ *     (((n * n_kv_heads + h) * (head_dim / x) + d / x) * block_size + t) * x + d % x
+ *   i.e. K is [num_blocks][n_kv_heads][head_dim / x][block_size][x]: each
+ *   token's key is cut into 16-byte rows of x consecutive dimensions.
+ *   V element (n, h, t, d) lives at element offset
+ *     ((n * n_kv_heads + h) * head_dim + d) * block_size + t
+ *   i.e. V is [num_blocks][n_kv_heads][head_dim][block_size].
+ * Keys are stored after RoPE.  FP8 codes hold value / scale.
+ */
+typedef struct pkv_pool_info {
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;          /* pkv_dtype */
+  int32_t kv_elem_bytes;
+  int32_t k_row_elems;       /* x above */
+  void* k_base;              /* device */
+  void* v_base;              /* device */
+  int64_t k_bytes;           /* bytes of K storage (equal for V) */
+  int64_t v_bytes;
+  const float* rope_cos;     /* device [rope_max_position][head_dim/2], or NULL */
+  const float* rope_sin;
+  int32_t rope_max_position; /* 0 until kv_pool_set_rope */
+  double rope_theta;
+  int32_t has_fp8_scales;
+  int32_t device;            /* HIP device ordinal */
+  int32_t n_waves;           /* wavefronts one decode_step launch runs */
+  int64_t workspace_bytes;
+} pkv_pool_info;
+
+/* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
+ * heads of head_dim dimensions in kv_dtype, on the current HIP device.
+ * Supported: head_dim in {64, 128}; block_size in {16, 32, 64};
+ * 1 <= n_kv_heads <= 256; 1 <= num_blocks < 2^31 and the pool at most 2^40
+ * bytes.
+ * Contents are left uninitialised.  On success *out_pool owns device memory
+ * until kv_pool_destroy.  Errors: INVALID (null/out of range), UNSUPPORTED,
+ * OOM, HIP. */
+pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size,
+                          int32_t n_kv_heads, int32_t head_dim,
+                          pkv_dtype kv_dtype, pkv_pool** out_pool);
+
+/* Free every device buffer of the pool (after synchronising its device).
+ * NULL is accepted and ignored. */
+pkv_status kv_pool_destroy(pkv_pool* pool);
+
+/* Build the RoPE table for positions [0, max_position): for i < head_dim/2,
+ * angle = p * theta^(-2i/head_dim) in double precision, cos and sin each
+ * rounded once to fp32 (rotate-half pairing (i, i + head_dim/2), as in
+ * "What Gets Fused" of "Scaling TensorRT-LLM: ...").  Synchronous.
+ * Errors: INVALID (theta <= 0, max_position < 1), OOM, HIP. */
+pkv_status kv_pool_set_rope(pkv_pool* pool, double theta, int32_t max_position);
+
+/* Set the FP8 scales (host arrays of n_kv_heads fp32 each, all > 0 and
+ * finite): a cached code c of head h means c * k_scale[h] (K) or
+ * c * v_scale[h] (V).  New tokens are encoded as E4M3(y * fp32(1/scale)) with
+ * round-to-nearest-even and saturation to +-448.  Synchronous.  Only for
+ * PKV_FP8_E4M3 pools (else INVALID). */
+pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, const float* k_scale,
+                                  const float* v_scale);
+
+/* Describe the pool (layout, device pointers). */
+pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info);
+
+/* One decode step for `batch` requests (asynchronous on `stream`, a
+ * hipStream_t; NULL = the default stream; no host synchronisation unless the
+ * environment variable PKV_DEBUG=1 asks for device-argument validation).
+ *
+ * Arguments (device pointers, contiguous, row-major; q, k_new, v_new and out
+ * 16-byte aligned, the int32 arrays 4-byte aligned):
+ *   q            [batch][n_q_heads][head_dim]   io_dtype, not rotated
+ *   k_new, v_new [batch][n_kv_heads][head_dim]  io_dtype, k_new not rotated
+ *   positions    [batch] int32   RoPE position of the new token
+ *   block_tables [batch][max_blocks_per_seq] int32 physical block ids
+ *   context_lens [batch] int32   L_b: tokens of request b counting the new one
+ *   out          [batch][n_q_heads][head_dim]   io_dtype (written)
+ * Effect: for each request b and KV head h, the rotated k_new and v_new are
+ * cast to kv_dtype and stored in slot L_b - 1 (block
+ * block_tables[b][(L_b-1)/block_size], offset (L_b-1) % block_size); then
+ * out[b][hq] = softmax over t < L_b of (rope(q[b][hq]) . K[t]) / sqrt(D),
+ * applied to V[t], with K/V read from head hq / (n_q_heads / n_kv_heads).
+ * Nothing else in the pool is written.
+ * Supported io/kv pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3);
+ * n_q_heads = G * n_kv_heads with 1 <= G <= 16; batch <= 4096.
+ * Caller guarantees (checked only under PKV_DEBUG=1; otherwise the kernel
+ * clamps out-of-range values, computes garbage for that request, and raises a
+ * flag readable with kv_pool_device_errors):
+ *   1 <= L_b <= max_blocks_per_seq * block_size;
+ *   entries 0 .. ceil(L_b/block_size)-1 of row b are ids in [0, num_blocks);
+ *   the block holding slot L_b-1 belongs to request b alone (other blocks may
+ *   be shared read-only between requests);
+ *   0 <= positions[b] < the RoPE max_position.
+ * The pool's workspace is shared: one decode_step at a time per pool.
+ * Every pointer must stay valid until the stream work completes.
+ * batch == 0 is a no-op.  Errors: INVALID, UNSUPPORTED, STATE (RoPE table or
+ * FP8 scales missing), HIP, DEVICE_DATA (debug validation). */
+pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
+                       const void* v_new, pkv_dtype io_dtype,
+                       const int32_t* positions, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t batch, int32_t n_q_heads, void* out,
+                       void* stream);
+
+/* Read and clear the device-side range flags raised by earlier decode_step
+ * calls (synchronises the device).  Bit 0: a block id outside
+ * [0, num_blocks); bit 1: a position outside [0, max_position); bit 2: a
+ * context length outside [1, max_blocks_per_seq * block_size]. */
+pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
+
+/* Tuning knobs (also read from PKV_WAVES_PER_CU and PKV_MIN_STEPS at pool
+ * creation).  waves_per_cu: resident wavefronts per compute unit the step
+ * is spread over (0 = from the kernel's occupancy); min_steps: fewest token
+ * steps a wavefront is given before fewer wavefronts are used (>= 1). */
+pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
+                              int32_t min_steps);
+
+/* Measurement.  While enabled, decode_step records HIP events on its launch
+ * stream before the attention kernel, between it and the split-merge kernel,
+ * and after the merge.  kv_pool_read_timing waits for the recorded events,
+ * returns the summed kernel milliseconds of each kind and the number of
+ * decode_step calls since the last read (or enable), and starts over.  At
+ * most 65536 calls are recorded between reads (later ones are not timed). */
+pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable);
+pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms,
+                               int32_t* calls);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ---- host-only helpers (no GPU needed) --------------------------------- */
+
+/* Check decode_step's host-visible arguments against a pool description,
+ * exactly as decode_step does before touching the GPU. */
+pkv_status pkv_check_decode_args(int64_t num_blocks, int32_t block_size,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 pkv_dtype kv_dtype, pkv_dtype io_dtype,
+                                 const void* q, const void* k_new,
+                                 const void* v_new, const int32_t* positions,
+                                 const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t n_q_heads, const void* out);
+
+/* The RoPE table kv_pool_set_rope uploads, computed into host arrays of
+ * max_position * head_dim/2 floats each. */
+pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
+                               int32_t max_position, float* cos_out,
+                               float* sin_out);
+
+/* The work partition decode_step's kernel computes on the device, replayed
+ * on the host from host copies of context_lens, for testing.  The batch's
+ * (request, KV head) sequences, each cut into steps of step_tokens tokens,
+ * are concatenated and split evenly over min(n_waves, ceil(N / min_steps))
+ * wavefronts.  Writes up to max_pieces rows of 6 int32 to pieces:
+ * {wave, request, kv_head, first_step, end_step, flags} with flags bit 0 =
+ * the piece is part of a split sequence, bit 1 = it is the wave's first piece,
+ * bit 2 = it is the last piece of its sequence; and n_waves rows of 4 int32 to
+ * headers (the reduce trigger each wave writes: {flags, sequence, first_wave,
+ * first_slot | pieces << 1}).  *n_pieces receives the total count. */
+pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
+                         int32_t n_kv_heads, int32_t step_tokens,
+                         int32_t max_tokens, int32_t n_waves, int32_t min_steps,
+                         int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
+                         int32_t* headers);
+
+/* Tokens per step of the kernel for a cache dtype (16 fp32, 32 bf16, 64 fp8). */
+int32_t pkv_step_tokens(pkv_dtype kv_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,310 @@
+"""Python binding of ``libpkv.so``, the paged-KV decode step for MI355X.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/pkv.h``.  PyTorch supplies
+device memory and the stream.  There is no fallback: if the library is not
+built, or no GPU is present, the calls raise.
+
+Names follow the C ABI: ``KVPool`` wraps ``kv_pool_*`` and ``decode_step``
+calls ``decode_step``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
+
+__all__ = [
+    "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
+    "check_decode_args", "rope_table_host", "plan_host", "step_tokens",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+_ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+_STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP",
+           -5: "STATE", -6: "DEVICE_DATA"}
+
+# every function include/pkv.h declares
+EXPORTED_SYMBOLS = (
+    "kv_pool_create", "kv_pool_destroy", "kv_pool_set_rope",
+    "kv_pool_set_fp8_scales", "kv_pool_get_info", "decode_step",
+    "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
+    "kv_pool_read_timing", "pkv_last_error",
+    "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
+    "pkv_step_tokens",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("kv_elem_bytes", ctypes.c_int32),
+        ("k_row_elems", ctypes.c_int32), ("k_base", ctypes.c_void_p),
+        ("v_base", ctypes.c_void_p), ("k_bytes", ctypes.c_int64),
+        ("v_bytes", ctypes.c_int64), ("rope_cos", ctypes.c_void_p),
+        ("rope_sin", ctypes.c_void_p), ("rope_max_position", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double), ("has_fp8_scales", ctypes.c_int32),
+        ("device", ctypes.c_int32), ("n_waves", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpkv.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise PkvError(-5, f"{path} is not built; run paged_kv_decode_step_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    IP = ctypes.POINTER(ctypes.c_int32)
+    FP = ctypes.POINTER(ctypes.c_float)
+    sig = {
+        "kv_pool_create": (I32, [I64, I32, I32, I32, I32, ctypes.POINTER(P)]),
+        "kv_pool_destroy": (I32, [P]),
+        "kv_pool_set_rope": (I32, [P, D, I32]),
+        "kv_pool_set_fp8_scales": (I32, [P, FP, FP]),
+        "kv_pool_get_info": (I32, [P, ctypes.POINTER(_Info)]),
+        "decode_step": (I32, [P, P, P, P, I32, P, P, I32, P, I32, I32, P, P]),
+        "kv_pool_device_errors": (I32, [P, ctypes.POINTER(ctypes.c_uint32)]),
+        "kv_pool_set_tuning": (I32, [P, I32, I32]),
+        "kv_pool_enable_timing": (I32, [P, I32]),
+        "kv_pool_read_timing": (I32, [P, ctypes.POINTER(D), ctypes.POINTER(D),
+                                      ctypes.POINTER(I32)]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_check_decode_args": (I32, [I64, I32, I32, I32, I32, I32, P, P, P, P, P,
+                                        I32, P, I32, I32, P]),
+        "pkv_rope_table_host": (I32, [D, I32, I32, FP, FP]),
+        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
+        "pkv_step_tokens": (I32, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PkvError(status, _lib.pkv_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+class _CudaArray:
+    """A device buffer described for torch.as_tensor (zero copy)."""
+
+    def __init__(self, ptr: int, shape, typestr: str):
+        self.__cuda_array_interface__ = {
+            "shape": tuple(int(s) for s in shape), "typestr": typestr,
+            "data": (int(ptr), False), "version": 2, "strides": None,
+        }
+
+
+class KVPool:
+    """Owner of a pool of KV blocks on the current device (``kv_pool_*``)."""
+
+    def __init__(self, num_blocks: int, block_size: int, n_kv_heads: int,
+                 head_dim: int, kv_dtype: str):
+        lib = load_library()
+        self.kv_dtype = kv_dtype
+        h = ctypes.c_void_p()
+        _check(lib.kv_pool_create(int(num_blocks), int(block_size), int(n_kv_heads),
+                                  int(head_dim), DTYPES[kv_dtype], ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.n_kv_heads, self.head_dim = int(n_kv_heads), int(head_dim)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise PkvError(-5, "pool is closed")
+        return self._h
+
+    def set_rope(self, theta: float, max_position: int) -> None:
+        _check(_lib.kv_pool_set_rope(self.handle, float(theta), int(max_position)))
+
+    def set_fp8_scales(self, k_scale: Sequence[float], v_scale: Sequence[float]) -> None:
+        n = self.n_kv_heads
+        ks = (ctypes.c_float * n)(*[float(x) for x in k_scale])
+        vs = (ctypes.c_float * n)(*[float(x) for x in v_scale])
+        _check(_lib.kv_pool_set_fp8_scales(self.handle, ks, vs))
+
+    def set_tuning(self, waves_per_cu: int = 0, min_steps: int = 4) -> None:
+        _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_steps)))
+
+    def enable_timing(self, enable: bool = True) -> None:
+        _check(_lib.kv_pool_enable_timing(self.handle, 1 if enable else 0))
+
+    def read_timing(self):
+        """(attention ms, merge ms, calls) summed since the last read."""
+        a, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+        _check(_lib.kv_pool_read_timing(self.handle, ctypes.byref(a), ctypes.byref(m),
+                                        ctypes.byref(n)))
+        return a.value, m.value, n.value
+
+    def info(self) -> dict:
+        inf = _Info()
+        _check(_lib.kv_pool_get_info(self.handle, ctypes.byref(inf)))
+        return {k: getattr(inf, k) for k, _ in _Info._fields_}
+
+    def device_errors(self) -> int:
+        f = ctypes.c_uint32()
+        _check(_lib.kv_pool_device_errors(self.handle, ctypes.byref(f)))
+        return int(f.value)
+
+    def _view(self, which: str):
+        inf = self.info()
+        ptr = inf["k_base"] if which == "k" else inf["v_base"]
+        nb, hk, bs, d = self.num_blocks, self.n_kv_heads, self.block_size, self.head_dim
+        e = _ELEM[self.kv_dtype]
+        x = 16 // e
+        shape = (nb, hk, d // x, bs, x) if which == "k" else (nb, hk, d, bs)
+        typestr = {4: "<f4", 2: "<i2", 1: "|u1"}[e]
+        t = torch.as_tensor(_CudaArray(ptr, shape, typestr), device=f"cuda:{inf['device']}")
+        return t
+
+    def k_storage(self):
+        """Raw K storage as a torch tensor view ``[nb, Hkv, D/x, bs, x]``
+        (float32 / int16 holding bf16 bits / uint8 E4M3 codes)."""
+        return self._view("k")
+
+    def v_storage(self):
+        """Raw V storage as a torch tensor view ``[nb, Hkv, D, bs]``."""
+        return self._view("v")
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            _lib.kv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
+                context_lens, out, stream=None) -> None:
+    """Launch one decode step (asynchronous on ``stream``; torch tensors).
+
+    ``q``/``out`` ``[B, Hq, D]``, ``k_new``/``v_new`` ``[B, Hkv, D]`` in the
+    I/O dtype (float32 or bfloat16), ``positions``/``context_lens`` int32
+    ``[B]``, ``block_tables`` int32 ``[B, max_blocks]``, all contiguous on the
+    pool's device.
+    """
+    lib = load_library()
+    io = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if io is None:
+        raise PkvError(-1, f"unsupported io dtype {q.dtype}")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("out", out),
+                    ("positions", positions), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise PkvError(-1, f"{name} must be contiguous")
+        if t.device.type != "cuda":
+            raise PkvError(-1, f"{name} must be on the GPU")
+    for name, t in (("positions", positions), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if t.dtype != torch.int32:
+            raise PkvError(-1, f"{name} must be int32")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("out", out)):
+        if t.dtype != q.dtype:
+            raise PkvError(-1, f"{name} must have q's dtype")
+    batch = int(q.shape[0])
+    hq = int(q.shape[1]) if q.dim() == 3 else 0
+    if q.dim() != 3 or q.shape[2] != pool.head_dim or out.shape != q.shape:
+        raise PkvError(-1, "q/out must be [B, Hq, head_dim]")
+    if tuple(k_new.shape) != (batch, pool.n_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
+        raise PkvError(-1, "k_new/v_new must be [B, Hkv, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise PkvError(-1, "block_tables must be [B, max_blocks]")
+    if positions.numel() != batch or context_lens.numel() != batch:
+        raise PkvError(-1, "positions/context_lens must be [B]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.decode_step(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), DTYPES[io],
+                           _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
+                           _ptr(context_lens), batch, hq, _ptr(out),
+                           ctypes.c_void_p(stream)))
+
+
+# ---- host-only helpers -----------------------------------------------------
+def step_tokens(kv_dtype: str) -> int:
+    return int(load_library().pkv_step_tokens(DTYPES[kv_dtype]))
+
+
+def check_decode_args(*, num_blocks, block_size, n_kv_heads, head_dim, kv_dtype,
+                      io_dtype, q=1, k_new=1, v_new=1, positions=1, block_tables=1,
+                      max_blocks_per_seq=1, context_lens=1, batch=1, n_q_heads=1,
+                      out=1) -> int:
+    """Run the library's host-side argument check; returns the status code.
+    Pointer arguments are plain integers (no memory is touched)."""
+    lib = load_library()
+    io = DTYPES.get(io_dtype, io_dtype) if isinstance(io_dtype, str) else io_dtype
+    kv = DTYPES.get(kv_dtype, kv_dtype) if isinstance(kv_dtype, str) else kv_dtype
+    return int(lib.pkv_check_decode_args(
+        int(num_blocks), int(block_size), int(n_kv_heads), int(head_dim), kv, io,
+        q, k_new, v_new, positions, block_tables, int(max_blocks_per_seq),
+        context_lens, int(batch), int(n_q_heads), out))
+
+
+def last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def rope_table_host(theta: float, head_dim: int, max_position: int):
+    """The library's RoPE table (numpy float32 ``[max_position, D/2]`` x2)."""
+    import numpy as np
+
+    lib = load_library()
+    n = max_position * (head_dim // 2)
+    c = np.empty(n, dtype=np.float32)
+    s = np.empty(n, dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    _check(lib.pkv_rope_table_host(float(theta), int(head_dim), int(max_position),
+                                   c.ctypes.data_as(fp), s.ctypes.data_as(fp)))
+    return c.reshape(max_position, head_dim // 2), s.reshape(max_position, head_dim // 2)
+
+
+def plan_host(context_lens, n_kv_heads: int, step: int, max_tokens: int,
+              n_waves: int, min_steps: int, max_pieces: int = 1 << 20):
+    """Host replay of the kernel's work partition (numpy arrays)."""
+    import numpy as np
+
+    lib = load_library()
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    pieces = np.zeros((max_pieces, 6), dtype=np.int32)
+    headers = np.zeros((n_waves, 4), dtype=np.int32)
+    n = ctypes.c_int32()
+    ip = ctypes.POINTER(ctypes.c_int32)
+    _check(lib.pkv_plan_host(lens.ctypes.data_as(ip), int(lens.shape[0]), int(n_kv_heads),
+                             int(step), int(max_tokens), int(n_waves), int(min_steps),
+                             int(max_pieces), pieces.ctypes.data_as(ip), ctypes.byref(n),
+                             headers.ctypes.data_as(ip)))
+    return pieces[:min(n.value, max_pieces)], headers

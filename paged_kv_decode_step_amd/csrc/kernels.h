@@ -1,0 +1,56 @@
+// kernels.h -- launch interface between the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kGroupMax = 16;      // query heads per KV head the kernel serves
+constexpr int kMaxBatch = 4096;    // requests per step (LDS prefix array)
+constexpr int kWaveThreads = 64;
+constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
+
+enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+struct DecodeParams {
+  const void* q;             // [B][Hq][D] io dtype
+  const void* k_new;         // [B][Hkv][D]
+  const void* v_new;
+  void* out;                 // [B][Hq][D]
+  const int32_t* positions;  // [B]
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* context_lens;  // [B]
+  void* k_pool;
+  void* v_pool;
+  const float* rope_cos;     // [max_pos][D/2]
+  const float* rope_sin;
+  const float* fp8_scales;   // [4][Hkv]: k_scale, v_scale, 1/k_scale, 1/v_scale
+  float* partials;           // [n_waves][2][kGroupMax][D + 2]
+  int4* headers;             // [n_waves]
+  uint32_t* err;             // [4] range flags
+  int32_t num_blocks;       // < 2^31 (checked at pool creation)
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t group;
+  int32_t max_blocks;        // block-table row length
+  int32_t max_pos;
+  int32_t n_waves;           // wavefronts launched (multiple of 4)
+  int32_t min_steps;
+  float sm_scale_log2;       // log2(e) / sqrt(D)
+};
+
+// Launch the fused append+attention kernel and the split-merge kernel on
+// `stream`; with `events` (3 of them) recorded before, between and after.
+hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
+                         hipStream_t stream, hipEvent_t* events);
+
+// Resident 256-thread workgroups per compute unit for the attention kernel.
+hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks_per_cu);
+
+// Bytes of workspace the kernels need for n_waves wavefronts.
+inline size_t partials_bytes(int n_waves, int head_dim) {
+  return (size_t)n_waves * 2 * kGroupMax * (head_dim + 2) * sizeof(float);
+}
+
+}  // namespace pkv

@@ -1,0 +1,558 @@
+// pkv_host.cpp -- the C ABI of include/pkv.h: pool ownership, RoPE table, FP8
+// scales, argument checks, the host replay of the work partition, launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(pkv_dtype t) {
+  switch (t) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+int kv_kind(pkv_dtype t) {
+  return t == PKV_F32 ? pkv::KV_F32 : (t == PKV_BF16 ? pkv::KV_BF16 : pkv::KV_FP8);
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+}  // namespace
+
+struct pkv_pool {
+  int device = 0;
+  int64_t num_blocks = 0;
+  int32_t block_size = 0, n_kv_heads = 0, head_dim = 0;
+  pkv_dtype kv_dtype = PKV_BF16;
+  void* k = nullptr;
+  void* v = nullptr;
+  int64_t kv_bytes = 0;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  int32_t rope_max_pos = 0;
+  double rope_theta = 0.0;
+  float* fp8_scales = nullptr;     // [4][Hkv]
+  bool has_scales = false;
+  float* partials = nullptr;
+  int4* headers = nullptr;
+  uint32_t* err = nullptr;
+  int64_t ws_bytes = 0;
+  int cus = 0;
+  int occ_blocks = 0;              // resident workgroups per CU (occupancy)
+  int waves_per_cu = 0;
+  int n_waves = 0;
+  int min_steps = 4;
+  // measurement: event triplets (before attention, between, after merge)
+  bool timing = false;
+  std::vector<hipEvent_t> events;
+  int timed_calls = 0;
+};
+
+static constexpr int kMaxTimedCalls = 65536;
+
+static void free_pool(pkv_pool* p) {
+  if (!p) return;
+  for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  (void)hipFree(p->k);
+  (void)hipFree(p->v);
+  (void)hipFree(p->rope_cos);
+  (void)hipFree(p->rope_sin);
+  (void)hipFree(p->fp8_scales);
+  (void)hipFree(p->partials);
+  (void)hipFree(p->headers);
+  (void)hipFree(p->err);
+  delete p;
+}
+
+static pkv_status size_workspace(pkv_pool* p, int waves_per_cu) {
+  int wpc = waves_per_cu > 0 ? waves_per_cu : p->occ_blocks * 4;
+  wpc = std::max(4, std::min(wpc, 32));
+  wpc = (wpc + 3) / 4 * 4;
+  const int n_waves = p->cus * wpc;
+  if (n_waves == p->n_waves && p->partials) return PKV_OK;
+  (void)hipFree(p->partials);
+  (void)hipFree(p->headers);
+  p->partials = nullptr;
+  p->headers = nullptr;
+  const size_t pb = pkv::partials_bytes(n_waves, p->head_dim);
+  hipError_t e = hipMalloc(&p->partials, pb);
+  if (e != hipSuccess) return fail(PKV_ERR_OOM, "workspace (%zu bytes): %s", pb, hipGetErrorString(e));
+  e = hipMalloc(&p->headers, sizeof(int4) * n_waves);
+  if (e != hipSuccess) return fail(PKV_ERR_OOM, "headers: %s", hipGetErrorString(e));
+  p->n_waves = n_waves;
+  p->waves_per_cu = wpc;
+  p->ws_bytes = (int64_t)pb + (int64_t)sizeof(int4) * n_waves;
+  return PKV_OK;
+}
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pkv_step_tokens(pkv_dtype kv_dtype) {
+  return 4 * (16 / std::max(1, elem_bytes(kv_dtype)));
+}
+
+pkv_status pkv_rope_table_host(double theta, int32_t head_dim, int32_t max_position,
+                               float* cos_out, float* sin_out) {
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(PKV_ERR_INVALID, "rope theta must be finite and > 0");
+  if (head_dim < 2 || head_dim % 2) return fail(PKV_ERR_INVALID, "head_dim must be even");
+  if (max_position < 1) return fail(PKV_ERR_INVALID, "max_position must be >= 1");
+  if (!cos_out || !sin_out) return fail(PKV_ERR_INVALID, "null output");
+  const int half = head_dim / 2;
+  std::vector<double> inv(half);
+  for (int i = 0; i < half; ++i) inv[i] = std::pow(theta, -(2.0 * i) / head_dim);
+  for (int64_t p = 0; p < max_position; ++p) {
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * inv[i];
+      cos_out[p * half + i] = (float)std::cos(ang);
+      sin_out[p * half + i] = (float)std::sin(ang);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                          int32_t head_dim, pkv_dtype kv_dtype, pkv_pool** out_pool) {
+  if (!out_pool) return fail(PKV_ERR_INVALID, "out_pool is null");
+  *out_pool = nullptr;
+  if (kv_dtype != PKV_F32 && kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID, "unknown kv_dtype %d", (int)kv_dtype);
+  if (num_blocks < 1 || num_blocks > INT32_MAX)
+    return fail(PKV_ERR_INVALID, "num_blocks must be in [1, 2^31)");
+  if (n_kv_heads < 1 || n_kv_heads > 256)
+    return fail(PKV_ERR_INVALID, "n_kv_heads must be in [1, 256]");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", head_dim);
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64)", block_size);
+  const int64_t per_block = (int64_t)n_kv_heads * block_size * head_dim * elem_bytes(kv_dtype);
+  if (num_blocks > ((int64_t)1 << 40) / per_block)
+    return fail(PKV_ERR_INVALID, "pool larger than 2^40 bytes");
+
+  pkv_pool* p = new pkv_pool();
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) { delete p; return hip_fail(e, "hipGetDevice"); }
+  e = hipDeviceGetAttribute(&p->cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) { delete p; return hip_fail(e, "hipDeviceGetAttribute"); }
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->n_kv_heads = n_kv_heads;
+  p->head_dim = head_dim;
+  p->kv_dtype = kv_dtype;
+  p->kv_bytes = num_blocks * per_block;
+  e = hipMalloc(&p->k, p->kv_bytes);
+  if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "K pool (%lld bytes): %s", (long long)per_block * num_blocks, hipGetErrorString(e)); }
+  e = hipMalloc(&p->v, p->kv_bytes);
+  if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "V pool: %s", hipGetErrorString(e)); }
+  e = hipMalloc(&p->err, 4 * sizeof(uint32_t));
+  if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "flags: %s", hipGetErrorString(e)); }
+  e = hipMemset(p->err, 0, 4 * sizeof(uint32_t));
+  if (e != hipSuccess) { free_pool(p); return hip_fail(e, "hipMemset"); }
+  e = hipMalloc(&p->fp8_scales, 4 * sizeof(float) * n_kv_heads);
+  if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "scales: %s", hipGetErrorString(e)); }
+  e = pkv::decode_occupancy(kv_kind(kv_dtype), head_dim, block_size, &p->occ_blocks);
+  if (e != hipSuccess) { free_pool(p); return hip_fail(e, "occupancy query"); }
+  p->occ_blocks = std::max(1, p->occ_blocks);
+  p->min_steps = std::max(1, env_int("PKV_MIN_STEPS", 4));
+  pkv_status s = size_workspace(p, env_int("PKV_WAVES_PER_CU", 0));
+  if (s != PKV_OK) { free_pool(p); return s; }
+  *out_pool = p;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_destroy(pkv_pool* pool) {
+  if (!pool) return PKV_OK;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(pool->device);
+  (void)hipDeviceSynchronize();
+  free_pool(pool);
+  (void)hipSetDevice(cur);
+  return PKV_OK;
+}
+
+pkv_status kv_pool_set_rope(pkv_pool* pool, double theta, int32_t max_position) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (max_position < 1 || max_position > (1 << 24))
+    return fail(PKV_ERR_INVALID, "max_position must be in [1, 2^24]");
+  const size_t n = (size_t)max_position * (pool->head_dim / 2);
+  std::vector<float> c(n), s(n);
+  pkv_status st = pkv_rope_table_host(theta, pool->head_dim, max_position, c.data(), s.data());
+  if (st != PKV_OK) return st;
+  (void)hipFree(pool->rope_cos);
+  (void)hipFree(pool->rope_sin);
+  pool->rope_cos = pool->rope_sin = nullptr;
+  pool->rope_max_pos = 0;
+  hipError_t e = hipMalloc(&pool->rope_cos, n * sizeof(float));
+  if (e != hipSuccess) return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+  e = hipMalloc(&pool->rope_sin, n * sizeof(float));
+  if (e != hipSuccess) return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+  e = hipMemcpy(pool->rope_cos, c.data(), n * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy rope");
+  e = hipMemcpy(pool->rope_sin, s.data(), n * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy rope");
+  pool->rope_max_pos = max_position;
+  pool->rope_theta = theta;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, const float* k_scale, const float* v_scale) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (pool->kv_dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID, "pool is not fp8");
+  if (!k_scale || !v_scale) return fail(PKV_ERR_INVALID, "null scale array");
+  const int h = pool->n_kv_heads;
+  std::vector<float> all(4 * h);
+  for (int i = 0; i < h; ++i) {
+    if (!(k_scale[i] > 0.f) || !std::isfinite(k_scale[i]) || !(v_scale[i] > 0.f) ||
+        !std::isfinite(v_scale[i]))
+      return fail(PKV_ERR_INVALID, "scale of head %d must be finite and > 0", i);
+    all[i] = k_scale[i];
+    all[h + i] = v_scale[i];
+    all[2 * h + i] = 1.0f / k_scale[i];
+    all[3 * h + i] = 1.0f / v_scale[i];
+  }
+  hipError_t e = hipMemcpy(pool->fp8_scales, all.data(), all.size() * sizeof(float),
+                           hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy scales");
+  pool->has_scales = true;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
+  if (!pool || !info) return fail(PKV_ERR_INVALID, "null argument");
+  std::memset(info, 0, sizeof *info);
+  info->num_blocks = pool->num_blocks;
+  info->block_size = pool->block_size;
+  info->n_kv_heads = pool->n_kv_heads;
+  info->head_dim = pool->head_dim;
+  info->kv_dtype = pool->kv_dtype;
+  info->kv_elem_bytes = elem_bytes(pool->kv_dtype);
+  info->k_row_elems = 16 / info->kv_elem_bytes;
+  info->k_base = pool->k;
+  info->v_base = pool->v;
+  info->k_bytes = pool->kv_bytes;
+  info->v_bytes = pool->kv_bytes;
+  info->rope_cos = pool->rope_cos;
+  info->rope_sin = pool->rope_sin;
+  info->rope_max_position = pool->rope_max_pos;
+  info->rope_theta = pool->rope_theta;
+  info->has_fp8_scales = pool->has_scales ? 1 : 0;
+  info->device = pool->device;
+  info->n_waves = pool->n_waves;
+  info->workspace_bytes = pool->ws_bytes;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_steps) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (min_steps < 1) return fail(PKV_ERR_INVALID, "min_steps must be >= 1");
+  if (waves_per_cu < 0 || waves_per_cu > 32)
+    return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(pool->device);
+  (void)hipDeviceSynchronize();
+  pkv_status s = size_workspace(pool, waves_per_cu);
+  (void)hipSetDevice(cur);
+  if (s != PKV_OK) return s;
+  pool->min_steps = min_steps;
+  return PKV_OK;
+}
+
+pkv_status pkv_check_decode_args(int64_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                                 int32_t head_dim, pkv_dtype kv_dtype, pkv_dtype io_dtype,
+                                 const void* q, const void* k_new, const void* v_new,
+                                 const int32_t* positions, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t batch, int32_t n_q_heads, const void* out) {
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch must be >= 0");
+  if (batch > pkv::kMaxBatch)
+    return fail(PKV_ERR_UNSUPPORTED, "batch %d above %d", batch, pkv::kMaxBatch);
+  if (io_dtype != PKV_F32 && io_dtype != PKV_BF16 && io_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID, "unknown io_dtype %d", (int)io_dtype);
+  const bool pair_ok = (io_dtype == PKV_F32 && kv_dtype == PKV_F32) ||
+                       (io_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
+                       (io_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3);
+  if (!pair_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "io/kv dtype pair (%d, %d) not supported", (int)io_dtype,
+                (int)kv_dtype);
+  if (n_kv_heads < 1) return fail(PKV_ERR_INVALID, "n_kv_heads must be >= 1");
+  if (n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return fail(PKV_ERR_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                n_q_heads, n_kv_heads);
+  const int g = n_q_heads / n_kv_heads;
+  if (g > pkv::kGroupMax)
+    return fail(PKV_ERR_UNSUPPORTED, "group size %d above %d", g, pkv::kGroupMax);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not supported", head_dim);
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not supported", block_size);
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "num_blocks must be >= 1");
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  if (cap > ((int64_t)1 << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size above 2^24 tokens");
+  const int64_t step = pkv_step_tokens(kv_dtype);
+  if ((int64_t)batch * n_kv_heads * ((cap + step - 1) / step) > ((int64_t)1 << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "batch * n_kv_heads * steps above 2^31");
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_new || !v_new || !positions || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_INVALID, "null device pointer");
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)k_new | (uintptr_t)v_new) % 16)
+    return fail(PKV_ERR_INVALID, "q, k_new, v_new and out must be 16-byte aligned");
+  if (((uintptr_t)positions | (uintptr_t)block_tables | (uintptr_t)context_lens) % 4)
+    return fail(PKV_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  return PKV_OK;
+}
+
+static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
+                                 const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t batch, hipStream_t stream) {
+  std::vector<int32_t> lens(batch), pos(batch), tab((size_t)batch * max_blocks);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  e = hipMemcpy(lens.data(), context_lens, batch * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(pos.data(), positions, batch * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess)
+    e = hipMemcpy(tab.data(), block_tables, tab.size() * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (debug validation)");
+  const int64_t cap = (int64_t)max_blocks * pool->block_size;
+  std::vector<int32_t> last_owner(pool->num_blocks, -1);
+  for (int b = 0; b < batch; ++b) {
+    if (lens[b] < 1 || lens[b] > cap)
+      return fail(PKV_ERR_DEVICE_DATA, "context_lens[%d] = %d outside [1, %lld]", b, lens[b],
+                  (long long)cap);
+    if (pos[b] < 0 || pos[b] >= pool->rope_max_pos)
+      return fail(PKV_ERR_DEVICE_DATA, "positions[%d] = %d outside [0, %d)", b, pos[b],
+                  pool->rope_max_pos);
+    const int nb = (lens[b] + pool->block_size - 1) / pool->block_size;
+    for (int j = 0; j < nb; ++j) {
+      const int32_t id = tab[(size_t)b * max_blocks + j];
+      if (id < 0 || id >= pool->num_blocks)
+        return fail(PKV_ERR_DEVICE_DATA, "block_tables[%d][%d] = %d outside [0, %lld)", b, j, id,
+                    (long long)pool->num_blocks);
+    }
+    const int32_t lb = tab[(size_t)b * max_blocks + nb - 1];
+    if (last_owner[lb] >= 0)
+      return fail(PKV_ERR_DEVICE_DATA,
+                  "block %d receives the new token of requests %d and %d", lb, last_owner[lb], b);
+    last_owner[lb] = b;
+  }
+  for (int b = 0; b < batch; ++b) {   // the appended block must not be read by others
+    const int nb = (lens[b] + pool->block_size - 1) / pool->block_size;
+    for (int j = 0; j < nb; ++j) {
+      const int32_t id = tab[(size_t)b * max_blocks + j];
+      if (last_owner[id] >= 0 && last_owner[id] != b)
+        return fail(PKV_ERR_DEVICE_DATA,
+                    "block %d is appended to by request %d and read by request %d", id,
+                    last_owner[id], b);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
+                       pkv_dtype io_dtype, const int32_t* positions, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                       int32_t n_q_heads, void* out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  pkv_status s = pkv_check_decode_args(pool->num_blocks, pool->block_size, pool->n_kv_heads,
+                                       pool->head_dim, pool->kv_dtype, io_dtype, q, k_new, v_new,
+                                       positions, block_tables, max_blocks_per_seq, context_lens,
+                                       batch, n_q_heads, out);
+  if (s != PKV_OK) return s;
+  if (batch == 0) return PKV_OK;
+  if (pool->rope_max_pos < 1) return fail(PKV_ERR_STATE, "kv_pool_set_rope was not called");
+  if (pool->kv_dtype == PKV_FP8_E4M3 && !pool->has_scales)
+    return fail(PKV_ERR_STATE, "kv_pool_set_fp8_scales was not called");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (env_int("PKV_DEBUG", 0) == 1) {
+    s = debug_validate(pool, positions, block_tables, max_blocks_per_seq, context_lens, batch, st);
+    if (s != PKV_OK) return s;
+  }
+  pkv::DecodeParams p;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.out = out;
+  p.positions = positions;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.k_pool = pool->k;
+  p.v_pool = pool->v;
+  p.rope_cos = pool->rope_cos;
+  p.rope_sin = pool->rope_sin;
+  p.fp8_scales = pool->fp8_scales;
+  p.partials = pool->partials;
+  p.headers = pool->headers;
+  p.err = pool->err;
+  p.num_blocks = (int32_t)pool->num_blocks;
+  p.batch = batch;
+  p.n_kv_heads = pool->n_kv_heads;
+  p.group = n_q_heads / pool->n_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_pos = pool->rope_max_pos;
+  p.n_waves = pool->n_waves;
+  p.min_steps = pool->min_steps;
+  p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
+  hipEvent_t* ev = nullptr;
+  if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
+    const size_t need = 3 * (size_t)(pool->timed_calls + 1);
+    while (pool->events.size() < need) {
+      hipEvent_t e;
+      hipError_t he = hipEventCreate(&e);
+      if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
+      pool->events.push_back(e);
+    }
+    ev = &pool->events[3 * (size_t)pool->timed_calls];
+    ++pool->timed_calls;
+  }
+  hipError_t e = pkv::launch_decode(kv_kind(pool->kv_dtype), pool->head_dim, pool->block_size, p,
+                                    st, ev);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return PKV_OK;
+}
+
+pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  pool->timing = enable != 0;
+  pool->timed_calls = 0;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms,
+                               int32_t* calls) {
+  if (!pool || !attn_ms || !merge_ms || !calls) return fail(PKV_ERR_INVALID, "null argument");
+  double a = 0.0, m = 0.0;
+  for (int i = 0; i < pool->timed_calls; ++i) {
+    hipEvent_t* ev = &pool->events[3 * (size_t)i];
+    hipError_t e = hipEventSynchronize(ev[2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float t0 = 0.f, t1 = 0.f;
+    e = hipEventElapsedTime(&t0, ev[0], ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, ev[1], ev[2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    a += t0;
+    m += t1;
+  }
+  *attn_ms = a;
+  *merge_ms = m;
+  *calls = pool->timed_calls;
+  pool->timed_calls = 0;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
+  if (!pool || !flags) return fail(PKV_ERR_INVALID, "null argument");
+  uint32_t f[4] = {0, 0, 0, 0};
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(f, pool->err, sizeof f, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(pool->err, 0, sizeof f);
+  if (e != hipSuccess) return hip_fail(e, "reading device flags");
+  *flags = (f[0] ? 1u : 0u) | (f[1] ? 2u : 0u) | (f[2] ? 4u : 0u);
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+                         int32_t step_tokens, int32_t max_tokens, int32_t n_waves,
+                         int32_t min_steps, int32_t max_pieces, int32_t* pieces,
+                         int32_t* n_pieces, int32_t* headers) {
+  if (!context_lens || !n_pieces || !headers || (max_pieces > 0 && !pieces))
+    return fail(PKV_ERR_INVALID, "null argument");
+  if (batch < 1 || n_kv_heads < 1 || step_tokens < 1 || n_waves < 1 || min_steps < 1 ||
+      max_tokens < 1)
+    return fail(PKV_ERR_INVALID, "sizes must be positive");
+  std::vector<int> P(batch + 1, 0);
+  for (int b = 0; b < batch; ++b)
+    P[b + 1] = P[b] + pkv::steps_of(context_lens[b], max_tokens, step_tokens);
+  const int64_t N = (int64_t)n_kv_heads * P[batch];
+  const int64_t We = pkv::active_waves(N, n_waves, min_steps);
+  int64_t count = 0;
+  for (int64_t w = 0; w < n_waves; ++w) {
+    int32_t* hdr = headers + 4 * w;
+    hdr[0] = hdr[1] = hdr[2] = hdr[3] = 0;
+    if (w >= We) continue;
+    const int64_t start = pkv::wave_start(w, N, We), end = pkv::wave_start(w + 1, N, We);
+    int b = pkv::find_request(P.data(), batch, start, n_kv_heads);
+    int ns = P[b + 1] - P[b];
+    int64_t rbase = (int64_t)n_kv_heads * P[b];
+    int h = (int)((start - rbase) / ns);
+    int64_t pos = start;
+    bool first = true;
+    while (pos < end) {
+      const int64_t sb = rbase + (int64_t)h * ns, se = sb + ns;
+      const int64_t pe = se < end ? se : end;
+      const bool split = sb < start || se > end;
+      if (count < max_pieces) {
+        int32_t* r = pieces + 6 * count;
+        r[0] = (int32_t)w;
+        r[1] = b;
+        r[2] = h;
+        r[3] = (int32_t)(pos - sb);
+        r[4] = (int32_t)(pe - sb);
+        r[5] = (split ? pkv::PIECE_SPLIT : 0) | (first ? pkv::PIECE_FIRST : 0) |
+               (pe == se ? pkv::PIECE_LAST : 0);
+      }
+      ++count;
+      if (first) {
+        if (split && se <= end) {
+          const int64_t wf = pkv::wave_of_step(sb, N, We);
+          hdr[0] = pkv::HDR_TRIGGER;
+          hdr[1] = b * n_kv_heads + h;
+          hdr[2] = (int32_t)wf;
+          hdr[3] = (pkv::wave_start(wf, N, We) == sb ? 0 : 1) | ((int)(w - wf + 1) << 1);
+        }
+        first = false;
+      }
+      pos = pe;
+      if (++h == n_kv_heads) {
+        h = 0;
+        if (++b < batch) {
+          ns = P[b + 1] - P[b];
+          rbase = (int64_t)n_kv_heads * P[b];
+        }
+      }
+    }
+  }
+  *n_pieces = (int32_t)std::min<int64_t>(count, INT32_MAX);
+  return PKV_OK;
+}
+
+}  // extern "C"

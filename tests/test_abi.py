@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: exports, host-side argument checks, the RoPE table,
+and the work partition the kernel computes (replayed on the host)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_decode_step_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, INVALID, UNSUPPORTED = 0, -1, -2
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_library_loads_and_exports_every_declared_function():
+    lib = pkv.load_library()
+    declared = header_functions()
+    assert set(declared) == set(pkv.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def base_args(**kw):
+    a = dict(num_blocks=100, block_size=16, n_kv_heads=8, head_dim=128, kv_dtype="bf16",
+             io_dtype="bf16", max_blocks_per_seq=64, batch=4, n_q_heads=32,
+             q=0x1000, k_new=0x2000, v_new=0x3000, positions=0x4000,
+             block_tables=0x5000, context_lens=0x6000, out=0x7000)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    {}, {"kv_dtype": "fp8"}, {"kv_dtype": "f32", "io_dtype": "f32"},
+    {"head_dim": 64}, {"block_size": 32}, {"block_size": 64},
+    {"n_q_heads": 8}, {"n_q_heads": 128}, {"batch": 4096}, {"batch": 0, "q": 0},
+])
+def test_check_accepts_supported(kw):
+    assert pkv.check_decode_args(**base_args(**kw)) == OK, pkv.last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"batch": -1}, INVALID),
+    ({"batch": 4097}, UNSUPPORTED),
+    ({"n_q_heads": 12}, INVALID),                # not a multiple of Hkv
+    ({"n_q_heads": 0}, INVALID),
+    ({"n_q_heads": 136}, UNSUPPORTED),           # group of 17
+    ({"head_dim": 96}, UNSUPPORTED),
+    ({"block_size": 8}, UNSUPPORTED),
+    ({"io_dtype": "f32"}, UNSUPPORTED),          # f32 io with bf16 cache
+    ({"kv_dtype": "f32"}, UNSUPPORTED),          # bf16 io with f32 cache
+    ({"io_dtype": 7}, INVALID),
+    ({"q": 0}, INVALID),
+    ({"context_lens": 0}, INVALID),
+    ({"out": 0x7004}, INVALID),                  # misaligned
+    ({"max_blocks_per_seq": 0}, INVALID),
+    ({"num_blocks": 0}, INVALID),
+    ({"max_blocks_per_seq": 1 << 21}, UNSUPPORTED),   # > 2^24 tokens
+])
+def test_check_rejects(kw, code):
+    assert pkv.check_decode_args(**base_args(**kw)) == code
+    assert pkv.last_error()
+
+
+def test_pool_create_validates_before_touching_the_gpu():
+    for args in [(0, 16, 8, 128, "bf16"), (10, 24, 8, 128, "bf16"),
+                 (10, 16, 0, 128, "bf16"), (10, 16, 8, 80, "bf16"),
+                 (1 << 40, 16, 8, 128, "bf16")]:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.KVPool(*args)
+        assert e.value.status in (INVALID, UNSUPPORTED)
+
+
+@pytest.mark.parametrize("theta,d", [(1.0e4, 64), (5.0e5, 128), (1.0e6, 128), (500.0, 64)])
+def test_rope_table_bit_equal_to_oracle(theta, d):
+    c, s = pkv.rope_table_host(theta, d, 9000)
+    positions = [0, 1, 2, 3, 137, 1011, 4095, 8191, 8999]
+    oc, os_ = oracle.rope_rows_f32(theta, d, positions)
+    assert np.array_equal(c[positions].view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s[positions].view(np.uint32), os_.view(np.uint32))
+
+
+def test_rope_table_rejects_bad_arguments():
+    with pytest.raises(pkv.PkvError):
+        pkv.rope_table_host(-1.0, 64, 10)
+    with pytest.raises(pkv.PkvError):
+        pkv.rope_table_host(1e4, 64, 0)
+
+
+def test_step_tokens():
+    assert pkv.step_tokens("f32") == 16
+    assert pkv.step_tokens("bf16") == 32
+    assert pkv.step_tokens("fp8") == 64
+
+
+# ---- work partition ---------------------------------------------------------
+def reference_partition(lens, hkv, step, cap, n_waves, min_steps):
+    """The partition written out plainly: sequences (b, h) in order, each cut
+    into max(1, ceil(min(L, cap)/step)) steps, then split evenly."""
+    ns = [max(1, -(-min(max(int(L), 0), cap) // step)) for L in lens]
+    seqs = [(b, h, ns[b]) for b in range(len(lens)) for h in range(hkv)]
+    total = sum(n for _, _, n in seqs)
+    we = min(n_waves, max(1, -(-total // min_steps)))
+    bounds = [(w * total) // we for w in range(we + 1)]
+    owner = {}
+    g = 0
+    for b, h, n in seqs:
+        for st in range(n):
+            w = max(i for i in range(we) if bounds[i] <= g)
+            owner[(b, h, st)] = w
+            g += 1
+    return owner, bounds, we, seqs
+
+
+@pytest.mark.parametrize("lens,hkv,step,waves,min_steps", [
+    ([138, 1012, 84], 4, 16, 64, 4),
+    ([1, 1, 1, 1], 2, 32, 64, 1),
+    ([5000, 3, 70, 31, 32, 33], 3, 32, 20, 2),
+    ([1], 1, 64, 8, 4),
+    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 32, 96, 3),
+    ([100] * 7, 2, 16, 1000, 1),          # more wavefronts than steps
+    ([0, -5, 40], 2, 32, 16, 1),          # invalid lengths still get one step
+])
+def test_partition_covers_every_step_once_and_balances(lens, hkv, step, waves, min_steps):
+    cap = 1 << 20
+    pieces, headers = pkv.plan_host(lens, hkv, step, cap, waves, min_steps)
+    owner, bounds, we, seqs = reference_partition(lens, hkv, step, cap, waves, min_steps)
+    seen = {}
+    per_wave = np.zeros(waves, dtype=np.int64)
+    for w, b, h, s0, s1, fl in pieces:
+        assert s0 < s1
+        for st in range(s0, s1):
+            assert (b, h, st) not in seen
+            seen[(b, h, st)] = w
+        per_wave[w] += s1 - s0
+    assert seen == owner
+    active = per_wave[:we]
+    assert active.min() >= 1 and active.max() - active.min() <= 1
+    assert np.all(per_wave[we:] == 0)
+    # flags and reduce headers against a direct reading
+    by_seq = {}
+    for w, b, h, s0, s1, fl in pieces:
+        by_seq.setdefault((b, h), []).append((w, s0, s1, fl))
+    trig = {}
+    for (b, h, n) in seqs:
+        ps = by_seq[(b, h)]
+        split = len(ps) > 1
+        for i, (w, s0, s1, fl) in enumerate(ps):
+            assert bool(fl & 1) == split
+            assert bool(fl & 4) == (s1 == n)
+        if split:
+            w_last = ps[-1][0]
+            w_first = ps[0][0]
+            first_is_first_piece = bool(ps[0][3] & 2)
+            trig[w_last] = (b * hkv + h, w_first, (0 if first_is_first_piece else 1) | (len(ps) << 1))
+            assert [p[0] for p in ps] == list(range(w_first, w_last + 1))
+    for w in range(waves):
+        hdr = headers[w]
+        if w in trig:
+            assert hdr[0] == 1 and tuple(hdr[1:]) == trig[w]
+        else:
+            assert hdr[0] == 0
