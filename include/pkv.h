@@ -63,15 +63,23 @@ typedef struct pkv_pool pkv_pool;
 
 /* Physical layout of the pool, for callers that fill or inspect it.
  *
- * x = 16 / kv_elem_bytes (4 for fp32, 8 for bf16, 16 for fp8).
- *   K element (block n, head h, slot t, dim d) lives at element offset
- *     (((n * n_kv_heads + h) * (head_dim / x) + d / x) * block_size + t) * x + d % x
- *   i.e. K is [num_blocks][n_kv_heads][head_dim / x][block_size][x]: each
- *   token's key is cut into 16-byte rows of x consecutive dimensions.
- *   V element (n, h, t, d) lives at element offset
- *     ((n * n_kv_heads + h) * head_dim + d) * block_size + t
- *   i.e. V is [num_blocks][n_kv_heads][head_dim][block_size].
- * Keys are stored after RoPE.  FP8 codes hold value / scale.
+ * A block of block_size tokens is cut into block_size / 16 tiles of 16
+ * tokens; for each (block n, KV head h, tile s) the tile's K and its V each
+ * fill T = 16 * head_dim * kv_elem_bytes contiguous bytes, a whole number of
+ * 1 KiB chunks.  With tpb = block_size / 16, the tile of (n, h, s) starts at
+ * byte ((n * n_kv_heads + h) * tpb + s) * T of k_base (K) and of v_base (V).
+ * Inside a tile, token t (0..15), dim d, element size E, x = 16 / E:
+ *   K: byte ((d / x) * 16 + t) * 16 + (d % x) * E
+ *      i.e. the tile is [head_dim / x][16 tokens][x]: 16-byte rows of x
+ *      consecutive dims of one token;
+ *   V: with g = 4 / E 16-dim groups per 16-byte row, nt = d / 16,
+ *      c = nt / g, k = nt % g:
+ *      byte ((c * 64 + (t / 4) * 16 + d % 16) * 16 + (4 * k + t % 4) * E
+ *      i.e. each 16-byte row holds tokens 4*(t/4) .. +3 of one dim in each of
+ *      g dim groups.
+ * These are the orders in which the matrix-core operands are read: each
+ * 16-byte row is one lane's share of one chunk.  Keys are stored after RoPE.
+ * FP8 codes hold value / scale.
  */
 typedef struct pkv_pool_info {
   int64_t num_blocks;
@@ -80,7 +88,7 @@ typedef struct pkv_pool_info {
   int32_t head_dim;
   int32_t kv_dtype;          /* pkv_dtype */
   int32_t kv_elem_bytes;
-  int32_t k_row_elems;       /* x above */
+  int32_t tile_bytes;        /* T above */
   void* k_base;              /* device */
   void* v_base;              /* device */
   int64_t k_bytes;           /* bytes of K storage (equal for V) */
@@ -149,6 +157,9 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info);
  * Nothing else in the pool is written.
  * Supported io/kv pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3);
  * n_q_heads = G * n_kv_heads with 1 <= G <= 16; batch <= 4096.
+ * Two kernels are launched: the fused append + attention kernel, and a small
+ * kernel that merges the partial softmax states of sequences split between
+ * wavefronts.
  * Caller guarantees (checked only under PKV_DEBUG=1; otherwise the kernel
  * clamps out-of-range values, computes garbage for that request, and raises a
  * flag readable with kv_pool_device_errors):
@@ -174,17 +185,19 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
  * context length outside [1, max_blocks_per_seq * block_size]. */
 pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 
-/* Tuning knobs (also read from PKV_WAVES_PER_CU and PKV_MIN_STEPS at pool
- * creation).  waves_per_cu: resident wavefronts per compute unit the step
- * is spread over (0 = from the kernel's occupancy); min_steps: fewest token
- * steps a wavefront is given before fewer wavefronts are used (>= 1). */
+/* Tuning knobs (also read from PKV_WAVES_PER_CU and PKV_MIN_TILES at pool
+ * creation).  waves_per_cu: wavefronts per compute unit the step is spread
+ * over (0 = as many as are resident at once, 8 on gfx950); min_tiles: fewest
+ * 16-token tiles a wavefront is given before fewer wavefronts are used
+ * (>= 1; default 16).  Synchronises the device. */
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
-                              int32_t min_steps);
+                              int32_t min_tiles);
 
 /* Measurement.  While enabled, decode_step records HIP events on its launch
  * stream before the attention kernel, between it and the split-merge kernel,
  * and after the merge.  kv_pool_read_timing waits for the recorded events,
- * returns the summed kernel milliseconds of each kind and the number of
+ * returns the summed milliseconds of each kind (event to event, so the merge
+ * figure includes the gap between the two launches) and the number of
  * decode_step calls since the last read (or enable), and starts over.  At
  * most 65536 calls are recorded between reads (later ones are not timed). */
 pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable);
@@ -216,22 +229,23 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
 
 /* The work partition decode_step's kernel computes on the device, replayed
  * on the host from host copies of context_lens, for testing.  The batch's
- * (request, KV head) sequences, each cut into steps of step_tokens tokens,
- * are concatenated and split evenly over min(n_waves, ceil(N / min_steps))
- * wavefronts.  Writes up to max_pieces rows of 6 int32 to pieces:
- * {wave, request, kv_head, first_step, end_step, flags} with flags bit 0 =
- * the piece is part of a split sequence, bit 1 = it is the wave's first piece,
- * bit 2 = it is the last piece of its sequence; and n_waves rows of 4 int32 to
- * headers (the reduce trigger each wave writes: {flags, sequence, first_wave,
- * first_slot | pieces << 1}).  *n_pieces receives the total count. */
+ * (request, KV head) sequences, each cut into 16-token tiles (at least one;
+ * lengths clamped to [0, max_tokens]), are concatenated and split evenly over
+ * min(n_waves, ceil(N / min_tiles)) wavefronts.  Writes up to max_pieces rows
+ * of 6 int32 to pieces: {wave, request, kv_head, first_tile, end_tile, flags}
+ * with flags bit 0 = the piece is part of a split sequence, bit 1 = it is the
+ * wave's first piece, bit 2 = it is the last piece of its sequence; and
+ * n_waves rows of 4 int32 to splits: row w describes the split sequence whose
+ * first piece wave w holds, {1, request * n_kv_heads + kv_head, pieces,
+ * partial slot of the first piece}, or zeros.  *n_pieces receives the total
+ * count. */
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
-                         int32_t n_kv_heads, int32_t step_tokens,
-                         int32_t max_tokens, int32_t n_waves, int32_t min_steps,
-                         int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
-                         int32_t* headers);
+                         int32_t n_kv_heads, int32_t max_tokens, int32_t n_waves,
+                         int32_t min_tiles, int32_t max_pieces, int32_t* pieces,
+                         int32_t* n_pieces, int32_t* splits);
 
-/* Tokens per step of the kernel for a cache dtype (16 fp32, 32 bf16, 64 fp8). */
-int32_t pkv_step_tokens(pkv_dtype kv_dtype);
+/* Tokens per tile, the kernel's unit of work (16). */
+int32_t pkv_tile_tokens(void);
 
 #ifdef __cplusplus
 }

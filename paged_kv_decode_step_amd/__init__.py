@@ -18,7 +18,7 @@ import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
 
 __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
-    "check_decode_args", "rope_table_host", "plan_host", "step_tokens",
+    "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
     "kv_pool_read_timing", "pkv_last_error",
     "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
-    "pkv_step_tokens",
+    "pkv_tile_tokens",
 )
 
 
@@ -51,7 +51,7 @@ class _Info(ctypes.Structure):
         ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32), ("kv_elem_bytes", ctypes.c_int32),
-        ("k_row_elems", ctypes.c_int32), ("k_base", ctypes.c_void_p),
+        ("tile_bytes", ctypes.c_int32), ("k_base", ctypes.c_void_p),
         ("v_base", ctypes.c_void_p), ("k_bytes", ctypes.c_int64),
         ("v_bytes", ctypes.c_int64), ("rope_cos", ctypes.c_void_p),
         ("rope_sin", ctypes.c_void_p), ("rope_max_position", ctypes.c_int32),
@@ -91,8 +91,8 @@ def load_library(path: str = LIB_PATH):
         "pkv_check_decode_args": (I32, [I64, I32, I32, I32, I32, I32, P, P, P, P, P,
                                         I32, P, I32, I32, P]),
         "pkv_rope_table_host": (I32, [D, I32, I32, FP, FP]),
-        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
-        "pkv_step_tokens": (I32, [I32]),
+        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
+        "pkv_tile_tokens": (I32, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -152,8 +152,8 @@ class KVPool:
         vs = (ctypes.c_float * n)(*[float(x) for x in v_scale])
         _check(_lib.kv_pool_set_fp8_scales(self.handle, ks, vs))
 
-    def set_tuning(self, waves_per_cu: int = 0, min_steps: int = 4) -> None:
-        _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_steps)))
+    def set_tuning(self, waves_per_cu: int = 0, min_tiles: int = 16) -> None:
+        _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_tiles)))
 
     def enable_timing(self, enable: bool = True) -> None:
         _check(_lib.kv_pool_enable_timing(self.handle, 1 if enable else 0))
@@ -176,23 +176,22 @@ class KVPool:
         return int(f.value)
 
     def _view(self, which: str):
+        from . import pool_io
+
         inf = self.info()
         ptr = inf["k_base"] if which == "k" else inf["v_base"]
-        nb, hk, bs, d = self.num_blocks, self.n_kv_heads, self.block_size, self.head_dim
-        e = _ELEM[self.kv_dtype]
-        x = 16 // e
-        shape = (nb, hk, d // x, bs, x) if which == "k" else (nb, hk, d, bs)
-        typestr = {4: "<f4", 2: "<i2", 1: "|u1"}[e]
-        t = torch.as_tensor(_CudaArray(ptr, shape, typestr), device=f"cuda:{inf['device']}")
-        return t
+        args = (self.num_blocks, self.n_kv_heads, self.block_size, self.head_dim, self.kv_dtype)
+        shape = pool_io.k_shape(*args) if which == "k" else pool_io.v_shape(*args)
+        typestr = {4: "<f4", 2: "<i2", 1: "|u1"}[_ELEM[self.kv_dtype]]
+        return torch.as_tensor(_CudaArray(ptr, shape, typestr), device=f"cuda:{inf['device']}")
 
     def k_storage(self):
-        """Raw K storage as a torch tensor view ``[nb, Hkv, D/x, bs, x]``
+        """Raw K storage as a torch tensor view ``[nb, Hkv, bs/16, D/x, 16, x]``
         (float32 / int16 holding bf16 bits / uint8 E4M3 codes)."""
         return self._view("k")
 
     def v_storage(self):
-        """Raw V storage as a torch tensor view ``[nb, Hkv, D, bs]``."""
+        """Raw V storage as a torch tensor view ``[nb, Hkv, bs/16, D/(16g), 4, 16, g, 4]``."""
         return self._view("v")
 
     def close(self) -> None:
@@ -255,8 +254,8 @@ def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
 
 
 # ---- host-only helpers -----------------------------------------------------
-def step_tokens(kv_dtype: str) -> int:
-    return int(load_library().pkv_step_tokens(DTYPES[kv_dtype]))
+def tile_tokens() -> int:
+    return int(load_library().pkv_tile_tokens())
 
 
 def check_decode_args(*, num_blocks, block_size, n_kv_heads, head_dim, kv_dtype,
@@ -292,19 +291,20 @@ def rope_table_host(theta: float, head_dim: int, max_position: int):
     return c.reshape(max_position, head_dim // 2), s.reshape(max_position, head_dim // 2)
 
 
-def plan_host(context_lens, n_kv_heads: int, step: int, max_tokens: int,
-              n_waves: int, min_steps: int, max_pieces: int = 1 << 20):
-    """Host replay of the kernel's work partition (numpy arrays)."""
+def plan_host(context_lens, n_kv_heads: int, max_tokens: int, n_waves: int,
+              min_tiles: int, max_pieces: int = 1 << 20):
+    """Host replay of the kernel's work partition (numpy arrays): pieces
+    ``[n, 6]`` and the per-wave split-sequence rows ``[n_waves, 4]``."""
     import numpy as np
 
     lib = load_library()
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     pieces = np.zeros((max_pieces, 6), dtype=np.int32)
-    headers = np.zeros((n_waves, 4), dtype=np.int32)
+    splits = np.zeros((n_waves, 4), dtype=np.int32)
     n = ctypes.c_int32()
     ip = ctypes.POINTER(ctypes.c_int32)
     _check(lib.pkv_plan_host(lens.ctypes.data_as(ip), int(lens.shape[0]), int(n_kv_heads),
-                             int(step), int(max_tokens), int(n_waves), int(min_steps),
-                             int(max_pieces), pieces.ctypes.data_as(ip), ctypes.byref(n),
-                             headers.ctypes.data_as(ip)))
-    return pieces[:min(n.value, max_pieces)], headers
+                             int(max_tokens), int(n_waves), int(min_tiles), int(max_pieces),
+                             pieces.ctypes.data_as(ip), ctypes.byref(n),
+                             splits.ctypes.data_as(ip)))
+    return pieces[:min(n.value, max_pieces)], splits

@@ -4,7 +4,7 @@
 // query and key, the append of the new K/V into the block pool, the gather of
 // the cached K/V through the block table, and softmax(q K^T / sqrt(D)) V with
 // an online softmax.  A second, small kernel merges the partial softmax
-// states of sequences that were cut between wavefronts.
+// states of the sequences that were cut between wavefronts (split-K).
 //
 // The pages ask for: the block-table lookup done inside the attention kernel
 // ("Scaling TensorRT-LLM: Kernel Fusion and Inflight Batching in Production",
@@ -13,36 +13,58 @@
 // Fused"); KV blocks read once and reused by every query head of the group
 // ("TensorRT-LLM Guide: High-Throughput GPU Inference Engine", section
 // "3. Custom Fused Attention Kernels: FMHA and XQA"); an E4M3 cache with
-// precomputed scales (same page, "4. Native FP8 Quantization on NVIDIA Hopper
-// & Blackwell"); attention and KV-cache update fused ("TensorRT-LLM" glossary,
-// inferensys.com, paragraph on the KV cache).
+// precomputed scales (same page, section "4. Native FP8 Quantization on NVIDIA
+// Hopper & Blackwell"); attention and KV-cache update fused ("TensorRT-LLM"
+// glossary, inferensys.com, paragraph on the KV cache).
 //
 // Mapping onto CDNA4.  The step streams the KV cache from HBM once per KV
-// head; the arithmetic is a G x D by D x T contraction (scores) and a G x T by
-// T x D one (values), G <= 16.  Both run on 16x16 MFMA tiles with the query
-// group padded to 16 columns: the matrix cores have ~40x more throughput than
-// the 8 TB/s stream needs even at 1/8 column use, while plain VALU FMAs would
-// use most of the vector ALU at G = 8.  Each 64-lane wavefront owns a
-// contiguous range of (request, KV head, token step) work (see plan.h) and
-// double-buffers whole steps of K and V (16 KiB per step) in registers:
-// 16-byte loads, no LDS round trip, in-order completion counters.
+// head, so it is bound by HBM bandwidth.  The unit of work is a tile: 16
+// tokens of one (request, KV head) sequence.  A tile's K and its V are each a
+// whole number of contiguous 1 KiB chunks inside one block, laid out so that
+// one 16-byte load per lane per chunk (all lanes of a wavefront at one
+// wave-uniform base) lands every element in the register the matrix cores
+// read it from: no LDS round trip and no shuffles on the data path.
 //
-// Register layouts (lane = 16 * lq + lr, lr in [0,16), lq in [0,4)).  For a
-// cache element of E bytes, X = 16 / E elements fill a 16-byte row, a step is
-// 4X tokens split into NG = X/4 sub-steps of 16 tokens.
-//  * Scores, sub-step g: A = K rows (16 tokens), B = rotated queries (16
-//    heads, zero beyond G), result lane (lr, lq) holds S[token X*lq + 4g + r]
-//    [head lr], r = 0..3.  A's row i is token X*(i/4) + 4g + i%4, so the same
-//    lane later holds exactly the probabilities the value product needs.
-//  * Contraction over d is order-free: lane (lr, lq) holds dims
-//    [X*(lq + 4j), X*(lq + 4j) + X) of its key row for j < D/(4X), which is
-//    one 16-byte row of the K layout [D/X][bs][X].
-//  * Values: A = V^T (16 dims x tokens), B = P^T (tokens x 16 heads); lane
-//    (lr, lq) holds tokens [X*lq, X*lq + X) of dim 16*nt + lr, one 16-byte
-//    row of the V layout [D][bs]; the result accumulates O^T so lane (lr, lq)
-//    holds O[head lr][dims 16*nt + 4*lq + r].
+// Each wavefront owns a contiguous range of tiles (plan.h) and keeps RING
+// tiles in flight in registers, refilling a slot as soon as it has been used;
+// the ring runs on across sequence boundaries.  Block ids come from the block
+// table through the scalar cache, one tile ahead of the loads that need
+// them, so the vector memory counter only ever tracks the KV stream.
+//
+// Arithmetic.  Scores are a 16-token x G-head product over D, values a
+// D x G product over 16 tokens, G <= 16: both go to 16x16 MFMA tiles with the
+// group padded to 16 columns (the matrix cores have far more throughput than
+// the KV stream needs; the VALU would be busy with the FMAs at G = 8).
+// Lane = 16 * lq + lr with lr in [0, 16), lq in [0, 4):
+//  * scores: A = K rows (row lr = token lr of the tile), B = rotated queries
+//    (column lr = head lr, zero past G); the contraction over the head
+//    dimension is order-free, so lane (lr, lq) supplies the X dims
+//    [X*(4c + lq), X*(4c + lq) + X) of chunk c, X = 16 bytes / element size;
+//    the result gives lane (lr, lq) S[tokens 4lq .. 4lq+3][head lr];
+//  * values: A = V^T (16 dims x 4 tokens per lane), B = P^T; lane (lr, lq)
+//    supplies tokens 4lq .. 4lq+3 of dim lr of each 16-dim group, exactly the
+//    probabilities it already holds; the result gives it
+//    O[head lr][dims 16*nt + 4lq .. 16*nt + 4lq + 3].
+// The four lanes of a head (lq = 0..3) combine maxima and sums with the
+// gfx950 permlane16/permlane32 swaps.
+//
+// Split merge.  The partial states are plain stores and are merged by a
+// second launch: the kernel boundary makes them visible across the eight
+// XCDs' L2 caches with one write-back, where a device-scope release inside
+// the kernel would write back an XCD's whole L2 once per wavefront.
+#include <utility>
+
 #include "kernels.h"
 #include "plan.h"
+
+// K+V bytes each wavefront keeps in flight (fp8 needs registers for the code
+// conversions, so it keeps a little less).
+#ifndef PKV_RING_BYTES
+#define PKV_RING_BYTES 32768
+#endif
+#ifndef PKV_RING_BYTES_FP8
+#define PKV_RING_BYTES_FP8 24576
+#endif
 
 namespace pkv {
 namespace {
@@ -50,26 +72,40 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-template <int KV> struct KvT;
-template <> struct KvT<KV_F32>  { static constexpr int ELEM = 4, X = 4; };
-template <> struct KvT<KV_BF16> { static constexpr int ELEM = 2, X = 8; };
-template <> struct KvT<KV_FP8>  { static constexpr int ELEM = 1, X = 16; };
-
-constexpr float kLog2e = 1.4426950408889634f;
+template <class F, int... Is>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
 
 // ---------------------------------------------------------------- scalars
 __device__ __forceinline__ float exp2_fast(float x) {
   return __builtin_amdgcn_exp2f(x);   // v_exp_f32; -inf -> 0
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int m) {
-  return __shfl_xor(v, m, 64);
+// Combine a value over the four lanes lr, lr+16, lr+32, lr+48 (the lanes of
+// one query head).  Every lane gets the same bits.
+__device__ __forceinline__ float max_over_lq(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+
+__device__ __forceinline__ float sum_over_lq(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // float32 -> bfloat16 bits, round to nearest even (finite), quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -97,22 +133,29 @@ __device__ __forceinline__ uint32_t fp8_encode(float v) {
   return sign | ((uint32_t)(e + 7) << 3) | m;
 }
 
-// Two E4M3 codes spread as bytes [c1, 0, c0, 0] -> two f16 holding
-// value * 2^-8, exactly (subnormals included).
+// Two E4M3 codes spread as bytes [0, c0, 0, c1] -> two f16 holding
+// value * 2^-8, exactly (subnormals included): the exponent and mantissa
+// bits shift into place and the bias difference is the factor.
 __device__ __forceinline__ uint32_t fp8x2_spread_to_f16x2(uint32_t s) {
   return ((s >> 1) & 0x3f803f80u) | (s & 0x80008000u);
 }
 
+// Four E4M3 codes (bytes of w, lowest first) -> four f16 (value * 2^-8).
+__device__ __forceinline__ f16x4_t fp8x4_to_f16x4(uint32_t w) {
+  u32x2_t r;
+  r[0] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x010c000cu));
+  r[1] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x030c020cu));
+  return __builtin_bit_cast(f16x4_t, r);
+}
+
 __device__ __forceinline__ void fp8x16_to_f16(u32x4_t c, f16x8_t& lo, f16x8_t& hi) {
   u32x4_t a, b;
-  a[0] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[0], 0x010c000cu));
-  a[1] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[0], 0x030c020cu));
-  a[2] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[1], 0x010c000cu));
-  a[3] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[1], 0x030c020cu));
-  b[0] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[2], 0x010c000cu));
-  b[1] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[2], 0x030c020cu));
-  b[2] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[3], 0x010c000cu));
-  b[3] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, c[3], 0x030c020cu));
+  const f16x4_t a0 = fp8x4_to_f16x4(c[0]), a1 = fp8x4_to_f16x4(c[1]);
+  const f16x4_t b0 = fp8x4_to_f16x4(c[2]), b1 = fp8x4_to_f16x4(c[3]);
+  const u32x2_t wa0 = __builtin_bit_cast(u32x2_t, a0), wa1 = __builtin_bit_cast(u32x2_t, a1);
+  const u32x2_t wb0 = __builtin_bit_cast(u32x2_t, b0), wb1 = __builtin_bit_cast(u32x2_t, b1);
+  a[0] = wa0[0]; a[1] = wa0[1]; a[2] = wa1[0]; a[3] = wa1[1];
+  b[0] = wb0[0]; b[1] = wb0[1]; b[2] = wb1[0]; b[3] = wb1[1];
   lo = __builtin_bit_cast(f16x8_t, a);
   hi = __builtin_bit_cast(f16x8_t, b);
 }
@@ -139,143 +182,14 @@ __device__ __forceinline__ float load_io(const void* base, int64_t idx) {
   }
 }
 
-// Encode one float into the cache storage type (bit pattern in the low bits).
-template <int KV>
-__device__ __forceinline__ uint32_t encode_kv(float y, float inv_scale) {
-  if constexpr (KV == KV_F32) return __float_as_uint(y);
-  else if constexpr (KV == KV_BF16) return bf16_rne(y);
-  else return fp8_encode(y * inv_scale);
-}
-
-// Zero the elements with index >= nv in a 16-byte row of E-byte elements.
-template <int ELEM>
-__device__ __forceinline__ u32x4_t keep_first(u32x4_t row, int nv) {
-  constexpr int EPD = 4 / ELEM;
-  constexpr uint32_t M = ELEM == 4 ? 0xffffffffu : (ELEM == 2 ? 0xffffu : 0xffu);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t keep = 0;
-#pragma unroll
-    for (int k = 0; k < EPD; ++k)
-      keep |= (i * EPD + k < nv) ? (M << (k * ELEM * 8)) : 0u;
-    row[i] &= keep;
-  }
-  return row;
-}
-
-// ---------------------------------------------------------------- kernel
-template <int KV, int D, int BS>
-struct Cfg {
-  static constexpr int ELEM = KvT<KV>::ELEM;
-  static constexpr int X = KvT<KV>::X;       // elements per 16-byte row
-  static constexpr int NG = X / 4;           // 16-token sub-steps per step
-  static constexpr int STEP = 4 * X;         // tokens per step
-  static constexpr int NJ = D / (4 * X);     // key rows per lane per sub-step
-  static constexpr int NC = D / 16;          // 16-byte K (and V) rows per lane
-  static constexpr int HALF = D / 2;
-  static constexpr bool IO_BF16 = KV != KV_F32;
-  static constexpr int LOG2BS = BS == 16 ? 4 : (BS == 32 ? 5 : 6);
-  static constexpr int NB = STEP > BS ? STEP / BS : 1;   // blocks per step
-  static constexpr int TW = 256;             // block-table window per wavefront
-  static_assert(X <= BS, "a 16-byte row of V must stay inside one block");
-};
-
-// One step's worth of K and V in registers.
-template <int NC>
-struct StepBuf {
-  u32x4_t k[NC];
-  u32x4_t v[NC];
-};
-
-// Per-piece state.
-struct PieceCtx {
-  const char* kpool;
-  const char* vpool;
-  const int32_t* trow;    // block-table row of the request
-  int* tw;                // this wavefront's block-table window in LDS
-  int kvh, L, n_used;
-  int blk_base;           // block index held in tw[0]
-};
-
-// Refill the LDS window with block ids [base, base + TW) of the request
-// (0 past the request's last block; ids outside the pool become 0 and raise
-// a flag).  Waits for its own loads: called once per piece and then only
-// every TW blocks.
-template <int TW>
-__device__ __forceinline__ void fill_window(PieceCtx& c, const DecodeParams& p, int base,
-                                            int lane) {
-  c.blk_base = base;
-  int v[TW / 64];
-#pragma unroll
-  for (int i = 0; i < TW / 64; ++i) {
-    const int idx = base + i * 64 + lane;
-    const int id = c.trow[idx < c.n_used ? idx : 0];
-    v[i] = idx < c.n_used ? id : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < TW / 64; ++i) {
-    const bool ok = (unsigned)v[i] < (unsigned)p.num_blocks;
-    if (!ok) p.err[0] = 1u;
-    c.tw[i * 64 + lane] = ok ? v[i] : 0;
-  }
-}
-
-// K rows of step st: lane row lr is token X*(lr/4) + 4g + lr%4 of sub-step g.
-// Slides the block-table window first when the step runs past it.
-template <int KV, int D, int BS>
-__device__ __forceinline__ void issue_k(StepBuf<Cfg<KV, D, BS>::NC>& buf, PieceCtx& c,
-                                        const DecodeParams& p, int st, int lr, int lq,
-                                        int lane) {
-  using C = Cfg<KV, D, BS>;
-  const int token0 = st * C::STEP;
-  const int fb = token0 >> C::LOG2BS;
-  if (fb + C::NB - c.blk_base > C::TW) fill_window<C::TW>(c, p, fb, lane);
-  const int64_t hk = (int64_t)p.n_kv_heads;
-#pragma unroll
-  for (int g = 0; g < C::NG; ++g) {
-    const int t = token0 + C::X * (lr >> 2) + 4 * g + (lr & 3);
-    const int ph = c.tw[(t >> C::LOG2BS) - c.blk_base];
-    const int slot = t & (BS - 1);
-    const char* base = c.kpool +
-        ((((int64_t)ph * hk + c.kvh) * (D / C::X) + lq) * BS + slot) * 16;
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-      buf.k[g * C::NJ + j] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(base + j * 4 * BS * 16));
-  }
-}
-
-// V rows of step st: lane holds tokens [X*lq, X*lq + X) of dims 16*nt + lr.
-// Uses the window as issue_k of the same step left it.
-template <int KV, int D, int BS>
-__device__ __forceinline__ void issue_v(StepBuf<Cfg<KV, D, BS>::NC>& buf, const PieceCtx& c,
-                                        const DecodeParams& p, int st, int lr, int lq) {
-  using C = Cfg<KV, D, BS>;
-  const int t0 = st * C::STEP + C::X * lq;
-  const int ph = c.tw[(t0 >> C::LOG2BS) - c.blk_base];
-  const int slot0 = t0 & (BS - 1);
-  const char* base = c.vpool +
-      ((((int64_t)ph * p.n_kv_heads + c.kvh) * D + lr) * BS + slot0) * C::ELEM;
-#pragma unroll
-  for (int nt = 0; nt < C::NC; ++nt)
-    buf.v[nt] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4_t*>(base + nt * 16 * BS * C::ELEM));
-}
-
-// Query operand of the score MFMA: the rotated query of head lr (zero if
-// lr >= G) at the dims lane (lr, lq) contracts over.
-template <int KV, int NJ> struct QOp;
-template <int NJ> struct QOp<KV_BF16, NJ> { bf16x8_t v[NJ]; };
-template <int NJ> struct QOp<KV_FP8, NJ>  { f16x8_t v[NJ][2]; };
-template <int NJ> struct QOp<KV_F32, NJ>  { float v[NJ][4]; };
-
-// X consecutive io-dtype elements starting at element `off` -> float.
-template <bool IO_BF16, int X>
-__device__ __forceinline__ void load_row_f32(const void* base, int64_t off, float (&out)[X]) {
+// N consecutive io-dtype elements starting at element `off` -> float.
+template <bool IO_BF16, int N>
+__device__ __forceinline__ void load_row_f32(const void* base, int64_t off, float (&out)[N]) {
   if constexpr (IO_BF16) {
+    static_assert(N % 8 == 0, "bf16 rows are read 16 bytes at a time");
     const u32x4_t* ptr = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + off);
 #pragma unroll
-    for (int i = 0; i < X / 8; ++i) {
+    for (int i = 0; i < N / 8; ++i) {
       const u32x4_t w = ptr[i];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -284,9 +198,10 @@ __device__ __forceinline__ void load_row_f32(const void* base, int64_t off, floa
       }
     }
   } else {
+    static_assert(N % 4 == 0, "f32 rows are read 16 bytes at a time");
     const f32x4_t* ptr = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(base) + off);
 #pragma unroll
-    for (int i = 0; i < X / 4; ++i) {
+    for (int i = 0; i < N / 4; ++i) {
       const f32x4_t w = ptr[i];
 #pragma unroll
       for (int k = 0; k < 4; ++k) out[4 * i + k] = w[k];
@@ -294,484 +209,684 @@ __device__ __forceinline__ void load_row_f32(const void* base, int64_t off, floa
   }
 }
 
-template <int X>
-__device__ __forceinline__ void load_f32(const float* ptr, float (&out)[X]) {
+template <int N>
+__device__ __forceinline__ void load_f32(const float* ptr, float (&out)[N]) {
 #pragma unroll
-  for (int i = 0; i < X / 4; ++i) {
+  for (int i = 0; i < N / 4; ++i) {
     const f32x4_t w = reinterpret_cast<const f32x4_t*>(ptr)[i];
 #pragma unroll
     for (int k = 0; k < 4; ++k) out[4 * i + k] = w[k];
   }
 }
 
-// One step: scores from the K rows, then (after the caller's hook has
-// reused the K registers for the next step) the online softmax and P V.
-template <int KV, int D, int BS, class AfterScores>
-__device__ __forceinline__ void compute_step(StepBuf<Cfg<KV, D, BS>::NC>& buf,
-                                             const QOp<KV, Cfg<KV, D, BS>::NJ>& qop,
-                                             f32x4_t (&acc)[Cfg<KV, D, BS>::NC], float& m_run,
-                                             float& l_run, float sscale, int L, int st,
-                                             bool last, int lq, AfterScores&& after_scores) {
+// Encode one float into the cache storage type (bit pattern in the low bits).
+template <int KV>
+__device__ __forceinline__ uint32_t encode_kv(float y, float inv_scale) {
+  if constexpr (KV == KV_F32) return __float_as_uint(y);
+  else if constexpr (KV == KV_BF16) return bf16_rne(y);
+  else return fp8_encode(y * inv_scale);
+}
+
+// ---------------------------------------------------------------- layout
+template <int KV, int D, int BS>
+struct Cfg {
+  static constexpr int ELEM = KV == KV_F32 ? 4 : (KV == KV_BF16 ? 2 : 1);
+  static constexpr int X = 16 / ELEM;          // elements per 16-byte row
+  static constexpr int KCH = D * ELEM / 64;    // 1 KiB chunks of K (and of V) per tile
+  static constexpr int NGR = 4 / ELEM;         // 16-dim groups per 16-byte V row
+  static constexpr int NT = D / 16;            // 16-dim groups of the output
+  static constexpr int HALF = D / 2;
+  static constexpr int KROWS = D / X;          // 16-byte rows of one token's key
+  static constexpr int TILE_BYTES = KCH * 1024;
+  static constexpr int TPB = BS / kTileTokens; // tiles per block
+  static constexpr int LOG2TPB = TPB == 1 ? 0 : (TPB == 2 ? 1 : 2);
+  static constexpr int RING0 = (KV == KV_FP8 ? PKV_RING_BYTES_FP8 : PKV_RING_BYTES) / (2 * TILE_BYTES);
+  static constexpr int RING = RING0 < 2 ? 2 : (RING0 > 16 ? 16 : RING0);
+  static constexpr bool IO_BF16 = KV != KV_F32;
+  static_assert(KCH >= 1 && KCH * 64 == D * ELEM, "tile must be whole 1 KiB chunks");
+  static_assert(TPB >= 1 && TPB <= 4, "block_size must be 16, 32 or 64");
+  static_assert((2 * RING - 1) * KCH <= 63, "in-flight loads must fit the vmcnt counter");
+};
+
+// Byte offset of K element (token t of the tile, dim d) inside the tile:
+// the tile is [D/X][16 tokens][X], i.e. chunk c, lane 16*lq + t holds dims
+// X*(4c + lq) .. + X - 1 of token t.
+// Byte offset of V element (t, d): with nt = d / 16, c = nt / NGR,
+// k = nt % NGR, lr = d % 16, lq = t / 4, e = t % 4, it is
+// (c*64 + lq*16 + lr)*16 + (4k + e)*ELEM, i.e. chunk c, lane 16*lq + lr holds
+// tokens 4lq .. 4lq+3 of dims 16*(NGR*c + k) + lr for k < NGR.
+template <int KV, int D, int BS>
+__device__ __forceinline__ int v_elem_offset(int t, int d) {
   using C = Cfg<KV, D, BS>;
-  const int token0 = st * C::STEP;
+  const int nt = d >> 4, c = nt / C::NGR, k = nt % C::NGR;
+  return ((c * 64 + (t >> 2) * 16 + (d & 15)) * 16) + (4 * k + (t & 3)) * C::ELEM;
+}
 
-  // Scores for the NG sub-steps.
-  float s[C::NG][4];
-#pragma unroll
-  for (int g = 0; g < C::NG; ++g) {
-    f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      const u32x4_t kr = buf.k[g * C::NJ + j];
-      if constexpr (KV == KV_BF16) {
-        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr),
-                                                     qop.v[j], a4, 0, 0, 0);
-      } else if constexpr (KV == KV_FP8) {
-        f16x8_t lo, hi;
-        fp8x16_to_f16(kr, lo, hi);
-        a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qop.v[j][0], a4, 0, 0, 0);
-        a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qop.v[j][1], a4, 0, 0, 0);
-      } else {
-        const f32x4_t kf = __builtin_bit_cast(f32x4_t, kr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          a4 = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qop.v[j][e], a4, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[g][r] = a4[r] * sscale;
-  }
-  after_scores();
+template <int KCH>
+struct TileRegs {
+  u32x4_t k[KCH];
+  u32x4_t v[KCH];
+};
 
-  if (last) {
-    // Tokens at or past L: scores are -inf (selected, never multiplied) and
-    // their values are zeroed, whatever the unused slots hold.
-#pragma unroll
-    for (int g = 0; g < C::NG; ++g)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (token0 + C::X * lq + 4 * g + r >= L) s[g][r] = -INFINITY;
-    const int nv = L - (token0 + C::X * lq);
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt) buf.v[nt] = keep_first<C::ELEM>(buf.v[nt], nv);
-  }
+// Query operand of the score MFMA: the rotated query of head lr (zero if
+// lr >= G) at the dims lane (lr, lq) contracts over in chunk c.
+template <int KV, int KCH> struct QOp;
+template <int KCH> struct QOp<KV_BF16, KCH> { bf16x8_t v[KCH]; };
+template <int KCH> struct QOp<KV_FP8, KCH>  { f16x8_t v[KCH][2]; };
+template <int KCH> struct QOp<KV_F32, KCH>  { float v[KCH][4]; };
 
-  // Online softmax over the step (log2 domain); the four lanes lq = 0..3 of
-  // head lr share one running max.
-  float mx = s[0][0];
-#pragma unroll
-  for (int g = 0; g < C::NG; ++g)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[g][r]);
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx);
-  const float mb = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = exp2_fast(m_run - mb);
-  m_run = m_new;
-  float ps = 0.f;
-#pragma unroll
-  for (int g = 0; g < C::NG; ++g)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[g][r] = exp2_fast(s[g][r] - mb);
-      ps += s[g][r];
-    }
-  l_run = __builtin_fmaf(l_run, alpha, ps);
-#pragma unroll
-  for (int nt = 0; nt < C::NC; ++nt) acc[nt] *= alpha;
+// Position in the concatenation of the wave's sequences (wave-uniform).
+struct Walk {
+  int b, h, j, n;   // request, KV head, tile in the sequence, tiles of the sequence
+};
 
-  // P V.
-  if constexpr (KV == KV_BF16) {
-    u32x4_t pb;
-    pb[0] = pack_bf16x2(s[0][0], s[0][1]);
-    pb[1] = pack_bf16x2(s[0][2], s[0][3]);
-    pb[2] = pack_bf16x2(s[1][0], s[1][1]);
-    pb[3] = pack_bf16x2(s[1][2], s[1][3]);
-    const bf16x8_t pbv = __builtin_bit_cast(bf16x8_t, pb);
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, buf.v[nt]),
-                                                        pbv, acc[nt], 0, 0, 0);
-  } else if constexpr (KV == KV_FP8) {
-    u32x4_t p0, p1;
-    p0[0] = pack_f16x2(s[0][0], s[0][1]);
-    p0[1] = pack_f16x2(s[0][2], s[0][3]);
-    p0[2] = pack_f16x2(s[1][0], s[1][1]);
-    p0[3] = pack_f16x2(s[1][2], s[1][3]);
-    p1[0] = pack_f16x2(s[2][0], s[2][1]);
-    p1[1] = pack_f16x2(s[2][2], s[2][3]);
-    p1[2] = pack_f16x2(s[3][0], s[3][1]);
-    p1[3] = pack_f16x2(s[3][2], s[3][3]);
-    const f16x8_t pa = __builtin_bit_cast(f16x8_t, p0);
-    const f16x8_t pc = __builtin_bit_cast(f16x8_t, p1);
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt) {
-      f16x8_t lo, hi;
-      fp8x16_to_f16(buf.v[nt], lo, hi);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, pa, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, pc, acc[nt], 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt) {
-      const f32x4_t vf = __builtin_bit_cast(f32x4_t, buf.v[nt]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], s[0][e], acc[nt], 0, 0, 0);
+__device__ __forceinline__ void walk_next(Walk& w, const int* sP, int B, int hkv) {
+  if (++w.j == w.n) {
+    w.j = 0;
+    if (++w.h == hkv) {
+      w.h = 0;
+      if (++w.b < B) w.n = uniform(sP[w.b + 1] - sP[w.b]);
     }
   }
 }
 
-// Append of the new token, done before the piece's loads are issued.  The
-// rotated key (pinned fp32 arithmetic: two separate multiplies and one add or
-// subtract, no contraction) and the value are cast to the cache type and
-// stored into slot L-1.  Each element is written by the lane that later loads
-// it in the last step's layout, so program order makes that load return it.
+// ---------------------------------------------------------------- kernel
 template <int KV, int D, int BS>
-__device__ __forceinline__ void append_token(const DecodeParams& p, const PieceCtx& c, int b,
-                                             int posn, int lr, int lq) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
+                        const int32_t* __restrict__ lens, const int32_t* __restrict__ poss,
+                        char* __restrict__ kpool, char* __restrict__ vpool) {
   using C = Cfg<KV, D, BS>;
-  const int L = c.L;
-  const int rel = (L - 1) & (C::STEP - 1);        // position in the last step
-  const int row_new = 4 * (rel / C::X) + (rel & 3);
-  int phn = c.trow[(L - 1) >> C::LOG2BS];
-  if ((unsigned)phn >= (unsigned)p.num_blocks) {
-    p.err[0] = 1u;
-    phn = 0;
-  }
-  const int slot_new = (L - 1) & (BS - 1);
-  const int64_t hk = (int64_t)p.n_kv_heads;
-  const int64_t row_off = ((int64_t)b * hk + c.kvh) * D;
-  const float* crow = p.rope_cos + (int64_t)posn * C::HALF;
-  const float* srow = p.rope_sin + (int64_t)posn * C::HALF;
-  float inv_k = 1.0f, inv_v = 1.0f;
-  if constexpr (KV == KV_FP8) {
-    inv_k = p.fp8_scales[2 * p.n_kv_heads + c.kvh];
-    inv_v = p.fp8_scales[3 * p.n_kv_heads + c.kvh];
-  }
-  char* kpool = const_cast<char*>(c.kpool);
-  char* vpool = const_cast<char*>(c.vpool);
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) {
-    const int d0 = C::X * (lq + 4 * j);
-    const bool lo = d0 < C::HALF;
-    const int pd0 = lo ? d0 + C::HALF : d0 - C::HALF;
-    const int i0 = lo ? d0 : pd0;
-    float x[C::X], xp[C::X], cs[C::X], sn[C::X];
-    load_row_f32<C::IO_BF16, C::X>(p.k_new, row_off + d0, x);
-    load_row_f32<C::IO_BF16, C::X>(p.k_new, row_off + pd0, xp);
-    load_f32<C::X>(crow + i0, cs);
-    load_f32<C::X>(srow + i0, sn);
-    uint32_t enc[C::X];
-#pragma unroll
-    for (int e = 0; e < C::X; ++e) {
-      // lo half: y = x*C - x[i+D/2]*S ; hi half: y = x*C + x[i-D/2]*S
-      const float a = x[e] * cs[e];
-      const float bb = xp[e] * sn[e];
-      const float y = lo ? a - bb : a + bb;
-      enc[e] = encode_kv<KV>(y, inv_k);
-    }
-    u32x4_t row;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int k = 0; k < 4 / C::ELEM; ++k) w |= enc[i * (4 / C::ELEM) + k] << (k * C::ELEM * 8);
-      row[i] = w;
-    }
-    if (lr == row_new) {
-      char* dst = kpool + ((((int64_t)phn * hk + c.kvh) * (D / C::X) + lq + 4 * j) * BS +
-                           slot_new) * 16;
-      *reinterpret_cast<u32x4_t*>(dst) = row;
-    }
-  }
-  uint32_t vbits[C::NC];
-#pragma unroll
-  for (int nt = 0; nt < C::NC; ++nt)
-    vbits[nt] = encode_kv<KV>(load_io<C::IO_BF16>(p.v_new, row_off + 16 * nt + lr), inv_v);
-  if (lq == rel / C::X) {
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt) {
-      const int d = 16 * nt + lr;
-      char* dst = vpool + ((((int64_t)phn * hk + c.kvh) * D + d) * BS + slot_new) * C::ELEM;
-      if constexpr (C::ELEM == 4) *reinterpret_cast<uint32_t*>(dst) = vbits[nt];
-      else if constexpr (C::ELEM == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)vbits[nt];
-      else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)vbits[nt];
-    }
-  }
-}
-
-template <int KV, int D, int BS>
-__device__ __forceinline__ void process_piece(const DecodeParams& p, int* tw, int b, int kvh,
-                                              int ns, int st0, int st1, bool split, int slot,
-                                              int64_t wave, int lane) {
-  using C = Cfg<KV, D, BS>;
-  const int lr = lane & 15, lq = lane >> 4;
-  const int G = p.group;
-  const int cap = p.max_blocks * BS;
-
-  const int Lraw = p.context_lens[b];
-  const bool len_ok = Lraw >= 1 && Lraw <= cap;
-  const int L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
-  int posn = p.positions[b];
-  const bool pos_ok = posn >= 0 && posn < p.max_pos;
-  posn = posn < 0 ? 0 : (posn >= p.max_pos ? p.max_pos - 1 : posn);
-  if (st0 == 0) {
-    if (!len_ok) p.err[2] = 1u;
-    if (!pos_ok) p.err[1] = 1u;
-  }
-
-  PieceCtx c;
-  c.kpool = static_cast<const char*>(p.k_pool);
-  c.vpool = static_cast<const char*>(p.v_pool);
-  c.trow = p.block_tables + (int64_t)b * p.max_blocks;
-  c.tw = tw;
-  c.kvh = kvh;
-  c.L = L;
-  c.n_used = (L + BS - 1) >> C::LOG2BS;
-
-  // Rotated query of head lr at this lane's dims (fp32).  Heads past G load
-  // head 0 of the group (a valid address) and are zeroed.
-  const int hq = kvh * G + (lr < G ? lr : 0);
-  const bool hvalid = lr < G;
-  const int64_t qrow = ((int64_t)b * (p.n_kv_heads * G) + hq) * D;
-  const float* crow = p.rope_cos + (int64_t)posn * C::HALF;
-  const float* srow = p.rope_sin + (int64_t)posn * C::HALF;
-  float qv[C::NJ][C::X];
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) {
-    const int d0 = C::X * (lq + 4 * j);
-    const bool lo = d0 < C::HALF;
-    const int pd0 = lo ? d0 + C::HALF : d0 - C::HALF;
-    const int i0 = lo ? d0 : pd0;
-    float x[C::X], xp[C::X], cs[C::X], sn[C::X];
-    load_row_f32<C::IO_BF16, C::X>(p.q, qrow + d0, x);
-    load_row_f32<C::IO_BF16, C::X>(p.q, qrow + pd0, xp);
-    load_f32<C::X>(crow + i0, cs);
-    load_f32<C::X>(srow + i0, sn);
-#pragma unroll
-    for (int e = 0; e < C::X; ++e) {
-      const float y = lo ? (x[e] * cs[e] - xp[e] * sn[e]) : (x[e] * cs[e] + xp[e] * sn[e]);
-      qv[j][e] = hvalid ? y : 0.0f;
-    }
-  }
-
-  if (len_ok && st1 == ns) append_token<KV, D, BS>(p, c, b, posn, lr, lq);
-
-  fill_window<C::TW>(c, p, (st0 * C::STEP) >> C::LOG2BS, lane);
-  StepBuf<C::NC> buf;
-  issue_k<KV, D, BS>(buf, c, p, st0, lr, lq, lane);
-  issue_v<KV, D, BS>(buf, c, p, st0, lr, lq);
-
-  float sscale = p.sm_scale_log2;
-  QOp<KV, C::NJ> qop;
-  if constexpr (KV == KV_BF16) {
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      u32x4_t w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(qv[j][2 * i], qv[j][2 * i + 1]);
-      qop.v[j] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  } else if constexpr (KV == KV_FP8) {
-    // Scale the query by a power of two so that it fits f16 with room to
-    // spare; the factor goes back into the score scale.
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < C::X; ++e) amax = fmaxf(amax, fabsf(qv[j][e]));
-    amax = fmaxf(amax, shfl_xor(amax, 16));
-    amax = fmaxf(amax, shfl_xor(amax, 32));
-    int ex = 0;
-    if (amax > 0.f) {
-      (void)__builtin_frexpf(amax, &ex);   // amax < 2^ex
-      ex = ex > 15 ? ex - 15 : 0;
-    }
-    const float qs = __builtin_ldexpf(1.0f, -ex);
-    sscale = p.sm_scale_log2 * p.fp8_scales[kvh] * __builtin_ldexpf(1.0f, 8 + ex);
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4_t w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = pack_f16x2(qv[j][8 * hh + 2 * i] * qs, qv[j][8 * hh + 2 * i + 1] * qs);
-        qop.v[j][hh] = __builtin_bit_cast(f16x8_t, w);
-      }
-  } else {
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qop.v[j][e] = qv[j][e];
-  }
-
-  f32x4_t acc[C::NC];
-#pragma unroll
-  for (int nt = 0; nt < C::NC; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // One buffer: the next step's K loads go out as soon as the scores are
-  // done, its V loads as soon as P V is done.
-  for (int st = st0; st < st1; ++st) {
-    const bool more = st + 1 < st1;
-    compute_step<KV, D, BS>(buf, qop, acc, m_run, l_run, sscale, L, st, st == ns - 1, lq,
-                            [&] { if (more) issue_k<KV, D, BS>(buf, c, p, st + 1, lr, lq, lane); });
-    if (more) issue_v<KV, D, BS>(buf, c, p, st + 1, lr, lq);
-  }
-
-  // Finish the piece: normalise and store, or leave a partial state.
-  float lt = l_run + shfl_xor(l_run, 16);
-  lt += shfl_xor(lt, 32);
-  float vsc = 1.0f;
-  if constexpr (KV == KV_FP8) vsc = 256.0f * p.fp8_scales[p.n_kv_heads + kvh];
-  if (!hvalid) return;
-  if (!split) {
-    const float inv = lt > 0.f ? vsc / lt : 0.f;
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt) {
-      const int d = 16 * nt + 4 * lq;
-      if constexpr (C::IO_BF16) {
-        u32x2_t w;
-        w[0] = bf16_rne(acc[nt][0] * inv) | (bf16_rne(acc[nt][1] * inv) << 16);
-        w[1] = bf16_rne(acc[nt][2] * inv) | (bf16_rne(acc[nt][3] * inv) << 16);
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + qrow + d) = w;
-      } else {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + qrow + d) = acc[nt] * inv;
-      }
-    }
-  } else {
-    float* part = p.partials + ((size_t)(wave * 2 + slot) * kGroupMax + lr) * (D + 2);
-#pragma unroll
-    for (int nt = 0; nt < C::NC; ++nt)
-      *reinterpret_cast<f32x4_t*>(part + 16 * nt + 4 * lq) = acc[nt] * vsc;
-    if (lq == 0) {
-      part[D] = m_run;
-      part[D + 1] = lt;
-    }
-  }
-}
-
-template <int KV, int D, int BS>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
-void decode_attn_kernel(DecodeParams p) {
-  using C = Cfg<KV, D, BS>;
+  constexpr int R = C::RING;
+  constexpr int PF = partial_floats(D);
   __shared__ int sP[kMaxBatch + 1];
-  __shared__ int sScan[kBlockThreads];
-  __shared__ int sTw[kBlockThreads / 64][C::TW];
+  __shared__ int sWsum[kBlockThreads / 64];
+  __shared__ u32x4_t sKrow[kBlockThreads / 64][C::KROWS];   // appended key row
+  __shared__ uint32_t sVrow[kBlockThreads / 64][D];          // appended value codes
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / 64) + (tid >> 6);
-  const int B = p.batch, hkv = p.n_kv_heads;
+  const int wid = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int B = p.batch, hkv = p.n_kv_heads, G = p.group;
   const int cap = p.max_blocks * BS;
 
-  // Steps per request, prefix-summed into LDS (every workgroup does this).
+  // ---- tiles per request, prefix-summed into LDS (every workgroup)
+  for (int i = tid; i < B; i += kBlockThreads) sP[i] = tiles_of(lens[i], cap);
+  __syncthreads();
   {
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int i0 = tid * per;
     int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int b = i0 + i;
-      if (b < B) sum += steps_of(p.context_lens[b], cap, C::STEP);
+    for (int i = 0; i < per; ++i)
+      if (i0 + i < B) sum += sP[i0 + i];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-    sScan[tid] = sum;
+    if (lane == 63) sWsum[wid] = incl;
     __syncthreads();
-    for (int off = 1; off < kBlockThreads; off <<= 1) {
-      const int v = tid >= off ? sScan[tid - off] : 0;
-      __syncthreads();
-      sScan[tid] += v;
-      __syncthreads();
-    }
-    int run = sScan[tid] - sum;
+    int run = incl - sum;
+    for (int w = 0; w < wid; ++w) run += sWsum[w];
     for (int i = 0; i < per; ++i) {
-      const int b = i0 + i;
-      if (b < B) {
-        sP[b] = run;
-        run += steps_of(p.context_lens[b], cap, C::STEP);
+      if (i0 + i < B) {
+        const int v = sP[i0 + i];
+        sP[i0 + i] = run;
+        run += v;
       }
     }
-    if (tid == kBlockThreads - 1) sP[B] = sScan[tid];
+    if (tid == kBlockThreads - 1) sP[B] = run;
     __syncthreads();
   }
 
   const int64_t N = (int64_t)hkv * sP[B];
-  const int64_t We = active_waves(N, p.n_waves, p.min_steps);
-  if (wave >= We) {
+  const int64_t W = active_waves(N, p.n_waves, p.min_tiles);
+  const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
+  if (wave >= W) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
     return;
   }
-  int* tw = sTw[tid >> 6];
-  const int64_t start = wave_start(wave, N, We);
-  const int64_t end = wave_start(wave + 1, N, We);
-  int b = find_request(sP, B, start, hkv);
-  int ns = sP[b + 1] - sP[b];
-  int64_t rbase = (int64_t)hkv * sP[b];
-  int h = (int)((start - rbase) / ns);
-  int64_t pos = start;
-  bool first = true;
-  while (pos < end) {
-    const int64_t seq_begin = rbase + (int64_t)h * ns;
-    const int64_t seq_end = seq_begin + ns;
-    const int64_t piece_end = seq_end < end ? seq_end : end;
-    const bool split = seq_begin < start || seq_end > end;
-    process_piece<KV, D, BS>(p, tw, b, h, ns, (int)(pos - seq_begin),
-                             (int)(piece_end - seq_begin), split, first ? 0 : 1, wave, lane);
-    if (first) {
-      if (lane == 0) {
-        int4 hdr = make_int4(0, 0, 0, 0);
-        if (split && seq_end <= end) {
-          const int64_t wf = wave_of_step(seq_begin, N, We);
-          const int slot_f = wave_start(wf, N, We) == seq_begin ? 0 : 1;
-          hdr = make_int4(HDR_TRIGGER, b * hkv + h, (int)wf,
-                          slot_f | ((int)(wave - wf + 1) << 1));
-        }
-        p.headers[wave] = hdr;
-      }
-      first = false;
+  const int64_t start = wave_start(wave, N, W);
+  const int T = uniform((int)(wave_start(wave + 1, N, W) - start));
+
+  Walk w0;
+  {
+    const int b = uniform(find_request(sP, B, start, hkv));
+    const int n = uniform(sP[b + 1] - sP[b]);
+    const int r = (int)(start - (int64_t)hkv * sP[b]);
+    w0.b = b;
+    w0.h = r / n;
+    w0.j = r - w0.h * n;
+    w0.n = n;
+  }
+
+  const int lane16 = lane * 16;
+  const char* dummy = static_cast<const char*>(p.dummy);
+  uint32_t bad_block = 0;
+
+  // ---- prefetch side: RING tiles in flight
+  TileRegs<C::KCH> ring[R];
+  Walk pw = w0;
+  int p_left = T;
+  auto load_blk = [&](const Walk& w) __attribute__((always_inline)) -> int {
+    return tables[(int64_t)w.b * p.max_blocks + (w.j >> C::LOG2TPB)];
+  };
+  int pf_blk = load_blk(pw);
+  int64_t pf_off = 0;
+  bool pf_live = false;
+
+  auto issue_k = [&](TileRegs<C::KCH>& t) __attribute__((always_inline)) {
+    pf_live = p_left > 0;
+    int blk = pf_blk;
+    if ((unsigned)blk >= (unsigned)p.num_blocks) {
+      bad_block |= pf_live ? 1u : 0u;
+      blk = 0;
     }
-    pos = piece_end;
-    if (++h == hkv) {
-      h = 0;
-      if (++b < B) {
-        ns = sP[b + 1] - sP[b];
-        rbase = (int64_t)hkv * sP[b];
+    pf_off = (((int64_t)blk * hkv + pw.h) * C::TPB + (pw.j & (C::TPB - 1))) * C::TILE_BYTES;
+    const char* base = pf_live ? kpool + pf_off : dummy;
+#pragma unroll
+    for (int c = 0; c < C::KCH; ++c)
+      t.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + c * 1024 + lane16));
+  };
+  auto issue_v = [&](TileRegs<C::KCH>& t) __attribute__((always_inline)) {
+    const char* base = pf_live ? vpool + pf_off : dummy;
+#pragma unroll
+    for (int c = 0; c < C::KCH; ++c)
+      t.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + c * 1024 + lane16));
+    if (pf_live) {
+      --p_left;
+      if (p_left > 0) {
+        walk_next(pw, sP, B, hkv);
+        pf_blk = load_blk(pw);
       }
+    }
+  };
+
+  static_for([&](auto U) __attribute__((always_inline)) {
+    issue_k(ring[decltype(U)::value]);
+    issue_v(ring[decltype(U)::value]);
+  }, std::make_integer_sequence<int, R>{});
+
+  // ---- consumer side
+  Walk cw = w0;
+  QOp<KV, C::KCH> qop;
+  f32x4_t acc[C::NT];
+  float m_run = -INFINITY, l_run = 0.f;
+  float sscale = p.sm_scale_log2, vsc = 1.0f;
+  int L = 1, pend = 1, slot = 0;
+  bool split = false, app = false;
+  int r0 = 0;
+  uint32_t bad_len = 0, bad_pos = 0;
+  int j0 = 0;
+  // the split sequence whose first piece this wavefront holds (its last piece)
+  int4 split_hdr = make_int4(0, 0, 0, 0);
+
+  const int64_t out_row_stride = (int64_t)hkv * G;   // query heads per request
+
+  auto begin_piece = [&](int i) __attribute__((always_inline)) {
+    const int b = cw.b, h = cw.h;
+    const int Lraw = lens[b];
+    int posn = poss[b];
+    const bool len_ok = Lraw >= 1 && Lraw <= cap;
+    const bool pos_ok = posn >= 0 && posn < p.max_pos;
+    bad_len |= len_ok ? 0u : 1u;
+    bad_pos |= pos_ok ? 0u : 1u;
+    posn = posn < 0 ? 0 : (posn >= p.max_pos ? p.max_pos - 1 : posn);
+    L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
+    j0 = cw.j;
+    pend = min(cw.n, j0 + (T - i));
+    split = j0 > 0 || pend < cw.n;
+    slot = i == 0 ? 0 : 1;
+    app = len_ok && pend == cw.n;
+
+    // Rotated query of head lr at this lane's dims (fp32 RoPE from the
+    // table).  Heads past G load head 0 of the group and are zeroed.
+    const int hq = h * G + (lr < G ? lr : 0);
+    const bool hvalid = lr < G;
+    const int64_t qrow = ((int64_t)b * out_row_stride + hq) * D;
+    const float* crow = p.rope_cos + (int64_t)posn * C::HALF;
+    const float* srow = p.rope_sin + (int64_t)posn * C::HALF;
+    // Chunks c and c + KCH/2 hold the two halves of the rotate-half pairs
+    // (dims d and d + D/2) and share one row of the cos/sin table; with a
+    // single chunk, lanes lq < 2 hold the lower half and lq >= 2 the upper.
+    constexpr int NPAIR = C::KCH >= 2 ? C::KCH / 2 : 1;
+    auto rotate_pair = [&](int c, float (&y0)[C::X], float (&y1)[C::X]) __attribute__((always_inline)) {
+      float x[C::X], xp[C::X], cs[C::X], sn[C::X];
+      if constexpr (C::KCH >= 2) {
+        const int d0 = C::X * (4 * c + lq);
+        load_row_f32<C::IO_BF16, C::X>(p.q, qrow + d0, x);
+        load_row_f32<C::IO_BF16, C::X>(p.q, qrow + d0 + C::HALF, xp);
+        load_f32<C::X>(crow + d0, cs);
+        load_f32<C::X>(srow + d0, sn);
+#pragma unroll
+        for (int e = 0; e < C::X; ++e) {
+          y0[e] = hvalid ? x[e] * cs[e] - xp[e] * sn[e] : 0.0f;
+          y1[e] = hvalid ? xp[e] * cs[e] + x[e] * sn[e] : 0.0f;
+        }
+      } else {
+        const int d0 = C::X * lq;
+        const bool lo = d0 < C::HALF;
+        const int pd0 = lo ? d0 + C::HALF : d0 - C::HALF;
+        const int i0 = lo ? d0 : pd0;
+        load_row_f32<C::IO_BF16, C::X>(p.q, qrow + d0, x);
+        load_row_f32<C::IO_BF16, C::X>(p.q, qrow + pd0, xp);
+        load_f32<C::X>(crow + i0, cs);
+        load_f32<C::X>(srow + i0, sn);
+#pragma unroll
+        for (int e = 0; e < C::X; ++e) {
+          const float y = lo ? (x[e] * cs[e] - xp[e] * sn[e]) : (x[e] * cs[e] + xp[e] * sn[e]);
+          y0[e] = hvalid ? y : 0.0f;
+          y1[e] = 0.0f;
+        }
+      }
+    };
+    sscale = p.sm_scale_log2;
+    vsc = 1.0f;
+    if constexpr (KV == KV_BF16) {
+#pragma unroll
+      for (int c = 0; c < NPAIR; ++c) {
+        float y0[C::X], y1[C::X];
+        rotate_pair(c, y0, y1);
+        u32x4_t w0, w1;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          w0[i2] = pack_bf16x2(y0[2 * i2], y0[2 * i2 + 1]);
+          w1[i2] = pack_bf16x2(y1[2 * i2], y1[2 * i2 + 1]);
+        }
+        qop.v[c] = __builtin_bit_cast(bf16x8_t, w0);
+        if constexpr (C::KCH >= 2) qop.v[c + NPAIR] = __builtin_bit_cast(bf16x8_t, w1);
+      }
+    } else if constexpr (KV == KV_FP8) {
+      // The query is scaled by a power of two so that it fits f16 with room
+      // to spare; the factor goes back into the score scale, with the K scale
+      // and the 2^-8 of the code conversion.  A rotation keeps each pair's
+      // norm, so |rotated| <= sqrt(2) * max |raw| bounds the scale from the
+      // raw row before anything is rotated.
+      float amax = 0.f;
+      {
+        const int d0 = C::X * lq;
+#pragma unroll
+        for (int c = 0; c < C::KCH; ++c) {
+          float x[C::X];
+          load_row_f32<C::IO_BF16, C::X>(p.q, qrow + d0 + 4 * C::X * c, x);
+#pragma unroll
+          for (int e = 0; e < C::X; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        }
+      }
+      amax = max_over_lq(amax) * 1.4142137f;
+      int ex = 0;
+      if (amax > 0.f) {
+        (void)__builtin_frexpf(amax, &ex);   // amax < 2^ex
+        ex = ex > 15 ? ex - 15 : 0;
+      }
+      const float qs = __builtin_ldexpf(1.0f, -ex);
+      sscale = p.sm_scale_log2 * p.fp8_scales[h] * __builtin_ldexpf(1.0f, 8 + ex);
+      vsc = 256.0f * p.fp8_scales[hkv + h];
+#pragma unroll
+      for (int c = 0; c < NPAIR; ++c) {
+        float y0[C::X], y1[C::X];
+        rotate_pair(c, y0, y1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4_t w0, w1;
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            w0[i2] = pack_f16x2(y0[8 * hh + 2 * i2] * qs, y0[8 * hh + 2 * i2 + 1] * qs);
+            w1[i2] = pack_f16x2(y1[8 * hh + 2 * i2] * qs, y1[8 * hh + 2 * i2 + 1] * qs);
+          }
+          qop.v[c][hh] = __builtin_bit_cast(f16x8_t, w0);
+          if constexpr (C::KCH >= 2) qop.v[c + NPAIR][hh] = __builtin_bit_cast(f16x8_t, w1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NPAIR; ++c) {
+        float y0[C::X], y1[C::X];
+        rotate_pair(c, y0, y1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qop.v[c][e] = y0[e];
+          if constexpr (C::KCH >= 2) qop.v[c + NPAIR][e] = y1[e];
+        }
+      }
+    }
+
+    // Append of the new token (slot L-1), when this piece ends the sequence.
+    // The rotated key uses the pinned fp32 arithmetic: two separate
+    // multiplies and one add or subtract, no contraction.  Both rows go to
+    // the pool and to LDS; the tile registers get them at the last tile, so
+    // it does not matter whether that tile's loads left before or after
+    // these stores.
+    if (app) {
+      r0 = (L - 1) & 15;
+      int blk = tables[(int64_t)b * p.max_blocks + (L - 1) / BS];
+      if ((unsigned)blk >= (unsigned)p.num_blocks) {
+        bad_block |= 1u;
+        blk = 0;
+      }
+      const int64_t toff = (((int64_t)blk * hkv + h) * C::TPB + (((L - 1) / kTileTokens) & (C::TPB - 1))) *
+                           C::TILE_BYTES;
+      const int64_t nrow = ((int64_t)b * hkv + h) * D;
+      float inv_k = 1.0f, inv_v = 1.0f;
+      if constexpr (KV == KV_FP8) {
+        inv_k = p.fp8_scales[2 * hkv + h];
+        inv_v = p.fp8_scales[3 * hkv + h];
+      }
+      if (lane < C::KROWS) {
+        const int d0 = C::X * lane;
+        const bool lo = d0 < C::HALF;
+        const int pd0 = lo ? d0 + C::HALF : d0 - C::HALF;
+        const int i0 = lo ? d0 : pd0;
+        float x[C::X], xp[C::X], cs[C::X], sn[C::X];
+        load_row_f32<C::IO_BF16, C::X>(p.k_new, nrow + d0, x);
+        load_row_f32<C::IO_BF16, C::X>(p.k_new, nrow + pd0, xp);
+        load_f32<C::X>(crow + i0, cs);
+        load_f32<C::X>(srow + i0, sn);
+        uint32_t enc[C::X];
+#pragma unroll
+        for (int e = 0; e < C::X; ++e) {
+          const float a = x[e] * cs[e];
+          const float bb = xp[e] * sn[e];
+          const float y = lo ? a - bb : a + bb;
+          enc[e] = encode_kv<KV>(y, inv_k);
+        }
+        u32x4_t row;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int k = 0; k < 4 / C::ELEM; ++k) w |= enc[i2 * (4 / C::ELEM) + k] << (k * C::ELEM * 8);
+          row[i2] = w;
+        }
+        *reinterpret_cast<u32x4_t*>(kpool + toff + (lane * 16 + r0) * 16) = row;
+        sKrow[wid][lane] = row;
+      }
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const int d = lane + 64 * k;
+        const uint32_t code = encode_kv<KV>(load_io<C::IO_BF16>(p.v_new, nrow + d), inv_v);
+        char* dst = vpool + toff + v_elem_offset<KV, D, BS>(r0, d);
+        if constexpr (C::ELEM == 4) *reinterpret_cast<uint32_t*>(dst) = code;
+        else if constexpr (C::ELEM == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)code;
+        else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)code;
+        sVrow[wid][d] = code;
+      }
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // Put the appended token into the registers of the sequence's last tile.
+  auto patch = [&](TileRegs<C::KCH>& t) __attribute__((always_inline)) {
+    if (lr == r0) {
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c) t.k[c] = sKrow[wid][4 * c + lq];
+    }
+    if (lq == (r0 >> 2)) {
+      const int e0 = r0 & 3;
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c)
+#pragma unroll
+        for (int k = 0; k < C::NGR; ++k) {
+          const uint32_t code = sVrow[wid][16 * (C::NGR * c + k) + lr];
+          const int byte = (4 * k + e0) * C::ELEM;
+          const int word = byte >> 2, sh = (byte & 3) * 8;
+          const uint32_t m = C::ELEM == 4 ? 0xffffffffu : ((1u << (8 * C::ELEM)) - 1u) << sh;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q == word) t.v[c][q] = (t.v[c][q] & ~m) | ((code << sh) & m);
+        }
+    }
+  };
+
+  auto scores = [&](const TileRegs<C::KCH>& t) __attribute__((always_inline)) -> f32x4_t {
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::KCH; ++c) {
+      if constexpr (KV == KV_BF16) {
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[c]),
+                                                    qop.v[c], a, 0, 0, 0);
+      } else if constexpr (KV == KV_FP8) {
+        f16x8_t lo, hi;
+        fp8x16_to_f16(t.k[c], lo, hi);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, qop.v[c][0], a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, qop.v[c][1], a, 0, 0, 0);
+      } else {
+        const f32x4_t kf = __builtin_bit_cast(f32x4_t, t.k[c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qop.v[c][e], a, 0, 0, 0);
+      }
+    }
+    return a;
+  };
+
+  // Online softmax over the tile (log2 domain) and P V.  On the sequence's
+  // last tile, tokens at or past L get score -inf (selected, never
+  // multiplied) and their values are zeroed, whatever the slots hold.
+  auto softmax_pv = [&](f32x4_t a, TileRegs<C::KCH>& t, bool last) __attribute__((always_inline)) {
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = a[r] * sscale;
+    if (last) {
+      const int nv = L - (16 * cw.j + 4 * lq);   // valid tokens among this lane's four
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r >= nv) s[r] = -INFINITY;
+      u32x4_t keep;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int by = 0; by < 4; ++by) {
+          const int e = ((4 * q + by) % (4 * C::ELEM)) / C::ELEM;   // token of byte
+          m |= (e < nv) ? (0xffu << (8 * by)) : 0u;
+        }
+        keep[q] = m;
+      }
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c) t.v[c] &= keep;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = max_over_lq(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float mb = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2_fast(m_run - mb);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r] = exp2_fast(s[r] - mb);
+      ps += s[r];
+    }
+    l_run = __builtin_fmaf(l_run, alpha, ps);
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) acc[nt] *= alpha;
+
+    if constexpr (KV == KV_BF16) {
+      u32x2_t pw2;
+      pw2[0] = pack_bf16x2(s[0], s[1]);
+      pw2[1] = pack_bf16x2(s[2], s[3]);
+      const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw2);
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          u32x2_t vw;
+          vw[0] = t.v[c][2 * k];
+          vw[1] = t.v[c][2 * k + 1];
+          acc[2 * c + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(s16x4_t, vw), pb, acc[2 * c + k], 0, 0, 0);
+        }
+    } else if constexpr (KV == KV_FP8) {
+      u32x2_t pw2;
+      pw2[0] = pack_f16x2(s[0], s[1]);
+      pw2[1] = pack_f16x2(s[2], s[3]);
+      const f16x4_t ph = __builtin_bit_cast(f16x4_t, pw2);
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[4 * c + k] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16x4(t.v[c][k]), ph,
+                                                                 acc[4 * c + k], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::KCH; ++c) {
+        const f32x4_t vf = __builtin_bit_cast(f32x4_t, t.v[c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], s[e], acc[c], 0, 0, 0);
+      }
+    }
+  };
+
+  auto store_out = [&](int b, int h, const f32x4_t (&o)[C::NT], float scale) __attribute__((always_inline)) {
+    if (lr >= G) return;
+    const int64_t row = ((int64_t)b * out_row_stride + h * G + lr) * D;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const int d = 16 * nt + 4 * lq;
+      if constexpr (C::IO_BF16) {
+        u32x2_t w;
+        w[0] = bf16_rne(o[nt][0] * scale) | (bf16_rne(o[nt][1] * scale) << 16);
+        w[1] = bf16_rne(o[nt][2] * scale) | (bf16_rne(o[nt][3] * scale) << 16);
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = w;
+      } else {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = o[nt] * scale;
+      }
+    }
+  };
+
+  auto end_piece = [&]() __attribute__((always_inline)) {
+    const float lt = sum_over_lq(l_run);
+    if (!split) {
+      store_out(cw.b, cw.h, acc, lt > 0.f ? vsc / lt : 0.f);
+      return;
+    }
+    float* part = p.partials + ((int64_t)wave * 2 + slot) * PF;
+    if (lr < G) {
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = acc[nt] * vsc;
+      if (lq == 0) {
+        part[16 * D + 2 * lr] = m_run;
+        part[16 * D + 2 * lr + 1] = lt;
+      }
+    }
+    if (j0 == 0) {
+      const int64_t sb = (int64_t)hkv * sP[cw.b] + (int64_t)cw.h * cw.n;
+      const int np = (int)(wave_of_tile(sb + cw.n - 1, N, W) - wave + 1);
+      split_hdr = make_int4(1, cw.b * hkv + cw.h, np, slot);
+    }
+  };
+
+  // ---- main loop: consume tile i from slot i % R, refill it with tile i + R.
+  // Loads are issued unconditionally (past the range they read the dummy
+  // buffer) so that the wait before each tile is a fixed count of the loads
+  // issued after it.
+  for (int base = 0; base < T; base += R) {
+    static_for([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int i = base + u;
+      const bool live = i < T;
+      if (live && (i == 0 || cw.j == 0)) begin_piece(i);
+      const bool last = cw.j == cw.n - 1;
+      if (live && last && app) patch(ring[u]);
+      const f32x4_t a = scores(ring[u]);
+      issue_k(ring[u]);
+      softmax_pv(a, ring[u], last);
+      issue_v(ring[u]);
+      if (live) {
+        if (i == T - 1 || last) end_piece();
+        walk_next(cw, sP, B, hkv);
+      }
+    }, std::make_integer_sequence<int, R>{});
+  }
+
+  if (bad_block | bad_len | bad_pos) {
+    if (lane == 0) {
+      if (bad_block) p.err[0] = 1u;
+      if (bad_pos) p.err[1] = 1u;
+      if (bad_len) p.err[2] = 1u;
     }
   }
+
+  if (lane == 0) p.headers[wave] = split_hdr;
 }
 
-// Merge the partial softmax states of each split sequence:
+// Merge the partial softmax states of each split sequence (one wavefront per
+// sequence, found from the header its first wavefront left):
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
+// Pieces are read four at a time, with the running maximum rescaling the
+// sums, so the loads of a batch are all in flight together.
 template <bool IO_BF16, int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
-  const int4 hdr = p.headers[blockIdx.x];
-  if (!(hdr.x & HDR_TRIGGER)) return;
-  const int hkv = p.n_kv_heads, G = p.group;
-  const int b = hdr.y / hkv, kvh = hdr.y % hkv;
-  const int wf = hdr.z, slot_f = hdr.w & 1, np = hdr.w >> 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += 128) {
-    const int hh = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int k = 0; k < np; ++k) {
-      const int slot = k == 0 ? slot_f : 0;
-      const float* part = p.partials + ((size_t)((wf + k) * 2 + slot) * kGroupMax + hh) * (D + 2);
-      M = fmaxf(M, part[D]);
+__global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParams p) {
+  constexpr int NT = D / 16;
+  constexpr int PF = partial_floats(D);
+  constexpr int KB = 4;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
+  const int4 hdr = p.headers[w];
+  if (!uniform(hdr.x)) return;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int G = p.group, hkv = p.n_kv_heads;
+  if (lr >= G) return;
+  const int seq = uniform(hdr.y), np = uniform(hdr.z), slot0 = uniform(hdr.w);
+  const int b = seq / hkv, h = seq - (seq / hkv) * hkv;
+  float M = -INFINITY, den = 0.f;
+  f32x4_t num[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) num[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < np; k0 += KB) {
+    float mk[KB], lk[KB];
+    f32x4_t ak[KB][NT];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int k = min(k0 + j, np - 1);
+      const float* part = p.partials + ((int64_t)(w + k) * 2 + (k == 0 ? slot0 : 0)) * PF;
+      mk[j] = part[16 * D + 2 * lr];
+      lk[j] = part[16 * D + 2 * lr + 1];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        ak[j][nt] = *reinterpret_cast<const f32x4_t*>(part + lane * (4 * NT) + 4 * nt);
     }
-    const float mb = M == -INFINITY ? 0.f : M;
-    float num = 0.f, den = 0.f;
-    for (int k = 0; k < np; ++k) {
-      const int slot = k == 0 ? slot_f : 0;
-      const float* part = p.partials + ((size_t)((wf + k) * 2 + slot) * kGroupMax + hh) * (D + 2);
-      const float f = exp2_fast(part[D] - mb);
-      num = __builtin_fmaf(f, part[d], num);
-      den = __builtin_fmaf(f, part[D + 1], den);
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (k0 + j < np) mb = fmaxf(mb, mk[j]);
+    const float base = mb == -INFINITY ? 0.f : mb;
+    const float sc = exp2_fast(M - base);
+    den *= sc;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) num[nt] *= sc;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (k0 + j < np) {
+        const float f = exp2_fast(mk[j] - base);
+        den = __builtin_fmaf(f, lk[j], den);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) num[nt] += f * ak[j][nt];
+      }
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    const int64_t oi = ((int64_t)b * (hkv * G) + kvh * G + hh) * D + d;
-    if constexpr (IO_BF16) static_cast<uint16_t*>(p.out)[oi] = (uint16_t)bf16_rne(o);
-    else static_cast<float*>(p.out)[oi] = o;
+    M = mb;
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const int64_t row = ((int64_t)b * hkv * G + h * G + lr) * D;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int d = 16 * nt + 4 * lq;
+    if constexpr (IO_BF16) {
+      u32x2_t o;
+      o[0] = bf16_rne(num[nt][0] * inv) | (bf16_rne(num[nt][1] * inv) << 16);
+      o[1] = bf16_rne(num[nt][2] * inv) | (bf16_rne(num[nt][3] * inv) << 16);
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = o;
+    } else {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = num[nt] * inv;
+    }
   }
 }
 
@@ -780,11 +895,12 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_attn_kernel<KV, D, BS>), dim3(p.n_waves / 4), dim3(kBlockThreads),
-                     0, stream, p);
+                     0, stream, p, p.block_tables, p.context_lens, p.positions,
+                     static_cast<char*>(p.k_pool), static_cast<char*>(p.v_pool));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<KV != KV_F32, D>), dim3(p.n_waves), dim3(128), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<KV != KV_F32, D>), dim3(p.n_waves / 4),
+                     dim3(kBlockThreads), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -10,6 +10,7 @@ constexpr int kGroupMax = 16;      // query heads per KV head the kernel serves
 constexpr int kMaxBatch = 4096;    // requests per step (LDS prefix array)
 constexpr int kWaveThreads = 64;
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
+constexpr int kTileTokens = 16;    // tokens per KV tile (the unit of work)
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -26,31 +27,39 @@ struct DecodeParams {
   const float* rope_cos;     // [max_pos][D/2]
   const float* rope_sin;
   const float* fp8_scales;   // [4][Hkv]: k_scale, v_scale, 1/k_scale, 1/v_scale
-  float* partials;           // [n_waves][2][kGroupMax][D + 2]
-  int4* headers;             // [n_waves]
+  float* partials;           // [n_waves][2][partial_floats(D)]
+  int4* headers;             // [n_waves] {split, request * Hkv + head, pieces, slot} of the
+                             // split sequence whose first piece the wavefront holds
+  const void* dummy;         // >= 8 KiB of readable device memory (tail loads)
   uint32_t* err;             // [4] range flags
-  int32_t num_blocks;       // < 2^31 (checked at pool creation)
+  int32_t num_blocks;        // < 2^31 (checked at pool creation)
   int32_t batch;
   int32_t n_kv_heads;
   int32_t group;
   int32_t max_blocks;        // block-table row length
   int32_t max_pos;
   int32_t n_waves;           // wavefronts launched (multiple of 4)
-  int32_t min_steps;
+  int32_t min_tiles;         // fewest tiles a wavefront is given
   float sm_scale_log2;       // log2(e) / sqrt(D)
 };
 
+// Floats of one partial softmax state: the accumulator of all 64 lanes
+// (lane-major, D/4 floats each) and a (max, sum) pair per query head.
+constexpr int partial_floats(int head_dim) { return 16 * head_dim + 2 * kGroupMax; }
+
 // Launch the fused append+attention kernel and the split-merge kernel on
-// `stream`; with `events` (3 of them) recorded before, between and after.
+// `stream`, with `events` (3 of them) recorded before, between and after.
 hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
                          hipStream_t stream, hipEvent_t* events);
 
 // Resident 256-thread workgroups per compute unit for the attention kernel.
 hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks_per_cu);
 
-// Bytes of workspace the kernels need for n_waves wavefronts.
+// Bytes of workspace the kernels need for n_waves wavefronts (partials).
 inline size_t partials_bytes(int n_waves, int head_dim) {
-  return (size_t)n_waves * 2 * kGroupMax * (head_dim + 2) * sizeof(float);
+  return (size_t)n_waves * 2 * partial_floats(head_dim) * sizeof(float);
 }
+
+constexpr size_t kDummyBytes = 16384;
 
 }  // namespace pkv

@@ -69,14 +69,15 @@ struct pkv_pool {
   float* fp8_scales = nullptr;     // [4][Hkv]
   bool has_scales = false;
   float* partials = nullptr;
-  int4* headers = nullptr;
+  int4* headers = nullptr;         // per-wave split records (attention -> merge)
+  void* dummy = nullptr;           // zeroed buffer read by loads past a wave's range
   uint32_t* err = nullptr;
   int64_t ws_bytes = 0;
   int cus = 0;
   int occ_blocks = 0;              // resident workgroups per CU (occupancy)
   int waves_per_cu = 0;
   int n_waves = 0;
-  int min_steps = 4;
+  int min_tiles = 16;
   // measurement: event triplets (before attention, between, after merge)
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -95,6 +96,7 @@ static void free_pool(pkv_pool* p) {
   (void)hipFree(p->fp8_scales);
   (void)hipFree(p->partials);
   (void)hipFree(p->headers);
+  (void)hipFree(p->dummy);
   (void)hipFree(p->err);
   delete p;
 }
@@ -109,6 +111,7 @@ static pkv_status size_workspace(pkv_pool* p, int waves_per_cu) {
   (void)hipFree(p->headers);
   p->partials = nullptr;
   p->headers = nullptr;
+  p->n_waves = 0;
   const size_t pb = pkv::partials_bytes(n_waves, p->head_dim);
   hipError_t e = hipMalloc(&p->partials, pb);
   if (e != hipSuccess) return fail(PKV_ERR_OOM, "workspace (%zu bytes): %s", pb, hipGetErrorString(e));
@@ -116,7 +119,7 @@ static pkv_status size_workspace(pkv_pool* p, int waves_per_cu) {
   if (e != hipSuccess) return fail(PKV_ERR_OOM, "headers: %s", hipGetErrorString(e));
   p->n_waves = n_waves;
   p->waves_per_cu = wpc;
-  p->ws_bytes = (int64_t)pb + (int64_t)sizeof(int4) * n_waves;
+  p->ws_bytes = (int64_t)pb + (int64_t)sizeof(int4) * n_waves + (int64_t)pkv::kDummyBytes;
   return PKV_OK;
 }
 
@@ -124,9 +127,7 @@ extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
-int32_t pkv_step_tokens(pkv_dtype kv_dtype) {
-  return 4 * (16 / std::max(1, elem_bytes(kv_dtype)));
-}
+int32_t pkv_tile_tokens(void) { return pkv::kTileTokens; }
 
 pkv_status pkv_rope_table_host(double theta, int32_t head_dim, int32_t max_position,
                                float* cos_out, float* sin_out) {
@@ -187,10 +188,14 @@ pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_h
   if (e != hipSuccess) { free_pool(p); return hip_fail(e, "hipMemset"); }
   e = hipMalloc(&p->fp8_scales, 4 * sizeof(float) * n_kv_heads);
   if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "scales: %s", hipGetErrorString(e)); }
+  e = hipMalloc(&p->dummy, pkv::kDummyBytes);
+  if (e != hipSuccess) { free_pool(p); return fail(PKV_ERR_OOM, "dummy buffer: %s", hipGetErrorString(e)); }
+  e = hipMemset(p->dummy, 0, pkv::kDummyBytes);
+  if (e != hipSuccess) { free_pool(p); return hip_fail(e, "hipMemset"); }
   e = pkv::decode_occupancy(kv_kind(kv_dtype), head_dim, block_size, &p->occ_blocks);
   if (e != hipSuccess) { free_pool(p); return hip_fail(e, "occupancy query"); }
   p->occ_blocks = std::max(1, p->occ_blocks);
-  p->min_steps = std::max(1, env_int("PKV_MIN_STEPS", 4));
+  p->min_tiles = std::max(1, env_int("PKV_MIN_TILES", 16));
   pkv_status s = size_workspace(p, env_int("PKV_WAVES_PER_CU", 0));
   if (s != PKV_OK) { free_pool(p); return s; }
   *out_pool = p;
@@ -264,7 +269,7 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->head_dim = pool->head_dim;
   info->kv_dtype = pool->kv_dtype;
   info->kv_elem_bytes = elem_bytes(pool->kv_dtype);
-  info->k_row_elems = 16 / info->kv_elem_bytes;
+  info->tile_bytes = 16 * pool->head_dim * info->kv_elem_bytes;
   info->k_base = pool->k;
   info->v_base = pool->v;
   info->k_bytes = pool->kv_bytes;
@@ -280,9 +285,9 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   return PKV_OK;
 }
 
-pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_steps) {
+pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_tiles) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
-  if (min_steps < 1) return fail(PKV_ERR_INVALID, "min_steps must be >= 1");
+  if (min_tiles < 1) return fail(PKV_ERR_INVALID, "min_tiles must be >= 1");
   if (waves_per_cu < 0 || waves_per_cu > 32)
     return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
   int cur = 0;
@@ -292,7 +297,7 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
   pkv_status s = size_workspace(pool, waves_per_cu);
   (void)hipSetDevice(cur);
   if (s != PKV_OK) return s;
-  pool->min_steps = min_steps;
+  pool->min_tiles = min_tiles;
   return PKV_OK;
 }
 
@@ -329,9 +334,9 @@ pkv_status pkv_check_decode_args(int64_t num_blocks, int32_t block_size, int32_t
   const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
   if (cap > ((int64_t)1 << 24))
     return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size above 2^24 tokens");
-  const int64_t step = pkv_step_tokens(kv_dtype);
-  if ((int64_t)batch * n_kv_heads * ((cap + step - 1) / step) > ((int64_t)1 << 31) - 1)
-    return fail(PKV_ERR_UNSUPPORTED, "batch * n_kv_heads * steps above 2^31");
+  const int64_t tile = pkv::kTileTokens;
+  if ((int64_t)batch * n_kv_heads * ((cap + tile - 1) / tile) > ((int64_t)1 << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "batch * n_kv_heads * tiles above 2^31");
   if (batch == 0) return PKV_OK;
   if (!q || !k_new || !v_new || !positions || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID, "null device pointer");
@@ -422,6 +427,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.fp8_scales = pool->fp8_scales;
   p.partials = pool->partials;
   p.headers = pool->headers;
+  p.dummy = pool->dummy;
   p.err = pool->err;
   p.num_blocks = (int32_t)pool->num_blocks;
   p.batch = batch;
@@ -430,7 +436,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.max_blocks = max_blocks_per_seq;
   p.max_pos = pool->rope_max_pos;
   p.n_waves = pool->n_waves;
-  p.min_steps = pool->min_steps;
+  p.min_tiles = pool->min_tiles;
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
@@ -491,33 +497,32 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
 }
 
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
-                         int32_t step_tokens, int32_t max_tokens, int32_t n_waves,
-                         int32_t min_steps, int32_t max_pieces, int32_t* pieces,
-                         int32_t* n_pieces, int32_t* headers) {
-  if (!context_lens || !n_pieces || !headers || (max_pieces > 0 && !pieces))
+                         int32_t max_tokens, int32_t n_waves, int32_t min_tiles,
+                         int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
+                         int32_t* splits) {
+  if (!context_lens || !n_pieces || !splits || (max_pieces > 0 && !pieces))
     return fail(PKV_ERR_INVALID, "null argument");
-  if (batch < 1 || n_kv_heads < 1 || step_tokens < 1 || n_waves < 1 || min_steps < 1 ||
-      max_tokens < 1)
+  if (batch < 1 || n_kv_heads < 1 || n_waves < 1 || min_tiles < 1 || max_tokens < 1)
     return fail(PKV_ERR_INVALID, "sizes must be positive");
   std::vector<int> P(batch + 1, 0);
-  for (int b = 0; b < batch; ++b)
-    P[b + 1] = P[b] + pkv::steps_of(context_lens[b], max_tokens, step_tokens);
+  for (int b = 0; b < batch; ++b) P[b + 1] = P[b] + pkv::tiles_of(context_lens[b], max_tokens);
   const int64_t N = (int64_t)n_kv_heads * P[batch];
-  const int64_t We = pkv::active_waves(N, n_waves, min_steps);
-  int64_t count = 0;
+  const int64_t W = pkv::active_waves(N, n_waves, min_tiles);
   for (int64_t w = 0; w < n_waves; ++w) {
-    int32_t* hdr = headers + 4 * w;
-    hdr[0] = hdr[1] = hdr[2] = hdr[3] = 0;
-    if (w >= We) continue;
-    const int64_t start = pkv::wave_start(w, N, We), end = pkv::wave_start(w + 1, N, We);
+    int32_t* row = splits + 4 * w;
+    row[0] = row[1] = row[2] = row[3] = 0;
+  }
+  int64_t count = 0;
+  for (int64_t w = 0; w < W; ++w) {
+    const int64_t start = pkv::wave_start(w, N, W), end = pkv::wave_start(w + 1, N, W);
     int b = pkv::find_request(P.data(), batch, start, n_kv_heads);
-    int ns = P[b + 1] - P[b];
+    int n = P[b + 1] - P[b];
     int64_t rbase = (int64_t)n_kv_heads * P[b];
-    int h = (int)((start - rbase) / ns);
+    int h = (int)((start - rbase) / n);
     int64_t pos = start;
     bool first = true;
     while (pos < end) {
-      const int64_t sb = rbase + (int64_t)h * ns, se = sb + ns;
+      const int64_t sb = rbase + (int64_t)h * n, se = sb + n;
       const int64_t pe = se < end ? se : end;
       const bool split = sb < start || se > end;
       if (count < max_pieces) {
@@ -531,21 +536,19 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
                (pe == se ? pkv::PIECE_LAST : 0);
       }
       ++count;
-      if (first) {
-        if (split && se <= end) {
-          const int64_t wf = pkv::wave_of_step(sb, N, We);
-          hdr[0] = pkv::HDR_TRIGGER;
-          hdr[1] = b * n_kv_heads + h;
-          hdr[2] = (int32_t)wf;
-          hdr[3] = (pkv::wave_start(wf, N, We) == sb ? 0 : 1) | ((int)(w - wf + 1) << 1);
-        }
-        first = false;
+      if (split && sb >= start) {       // the sequence starts here: wave w is its first
+        int32_t* row = splits + 4 * w;
+        row[0] = 1;
+        row[1] = b * n_kv_heads + h;
+        row[2] = (int32_t)(pkv::wave_of_tile(se - 1, N, W) - w + 1);
+        row[3] = pkv::first_piece_slot(sb, w, N, W);
       }
+      first = false;
       pos = pe;
       if (++h == n_kv_heads) {
         h = 0;
         if (++b < batch) {
-          ns = P[b + 1] - P[b];
+          n = P[b + 1] - P[b];
           rbase = (int64_t)n_kv_heads * P[b];
         }
       }

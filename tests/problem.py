@@ -1,14 +1,9 @@
 """Test-side construction of a decode-step problem on the host.
 
 Draws the seeded raw values of a workload and encodes them into cache and
-I/O storage with the oracle's codecs.  Also converts between the oracle's
-logical cache layout ``[num_blocks, Hkv, bs, D]`` and the library's physical
-layout, which the library's header defines as:
-
-* K: ``[num_blocks, Hkv, D / x, bs, x]`` with ``x = 16 / element_size``
-  (16-byte rows of ``x`` consecutive dimensions);
-* V: ``[num_blocks, Hkv, D, bs]`` (the block's tokens contiguous per
-  dimension).
+I/O storage with the oracle's codecs.  Also restates, from the library
+header's byte-offset formulas, where each element of the oracle's logical
+cache layout ``[num_blocks, Hkv, bs, D]`` lives in the library's pool.
 """
 from __future__ import annotations
 
@@ -85,30 +80,31 @@ def oracle_step(wl, arrs) -> dict:
         k_scale=arrs["k_scale"], v_scale=arrs["v_scale"])
 
 
-# ---- physical layout of the library ----------------------------------------
-def k_to_physical(kp: np.ndarray, kv_dtype: str) -> np.ndarray:
-    nb, hkv, bs, d = kp.shape
-    x = 16 // ELEM[kv_dtype]
-    return np.ascontiguousarray(
-        kp.reshape(nb, hkv, bs, d // x, x).transpose(0, 1, 3, 2, 4))
+# ---- physical layout of the library, restated from include/pkv.h ----------
+def k_elem_index(n, h, t, d, *, hkv, bs, head_dim, kv_dtype):
+    """Element index in the K pool of (block n, head h, token t, dim d),
+    from the byte-offset formula of the library header."""
+    e = ELEM[kv_dtype]
+    x = 16 // e
+    tpb = bs // 16
+    tile_bytes = 16 * head_dim * e
+    base = ((n * hkv + h) * tpb + t // 16) * tile_bytes
+    off = ((d // x) * 16 + t % 16) * 16 + (d % x) * e
+    return (base + off) // e
 
 
-def k_from_physical(kphys: np.ndarray, kv_dtype: str, bs: int, d: int) -> np.ndarray:
-    x = 16 // ELEM[kv_dtype]
-    nb, hkv = kphys.shape[:2]
-    return np.ascontiguousarray(
-        kphys.reshape(nb, hkv, d // x, bs, x).transpose(0, 1, 3, 2, 4)
-        .reshape(nb, hkv, bs, d))
-
-
-def v_to_physical(vp: np.ndarray) -> np.ndarray:
-    return np.ascontiguousarray(vp.transpose(0, 1, 3, 2))
-
-
-def v_from_physical(vphys: np.ndarray, bs: int, d: int) -> np.ndarray:
-    nb, hkv = vphys.shape[:2]
-    return np.ascontiguousarray(
-        vphys.reshape(nb, hkv, d, bs).transpose(0, 1, 3, 2))
+def v_elem_index(n, h, t, d, *, hkv, bs, head_dim, kv_dtype):
+    """Element index in the V pool of (block n, head h, token t, dim d)."""
+    e = ELEM[kv_dtype]
+    g = 4 // e
+    tpb = bs // 16
+    tile_bytes = 16 * head_dim * e
+    base = ((n * hkv + h) * tpb + t // 16) * tile_bytes
+    nt = d // 16
+    c, k = nt // g, nt % g
+    t16 = t % 16
+    off = (c * 64 + (t16 // 4) * 16 + d % 16) * 16 + (4 * k + t16 % 4) * e
+    return (base + off) // e
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

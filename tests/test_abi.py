@@ -95,76 +95,78 @@ def test_rope_table_rejects_bad_arguments():
         pkv.rope_table_host(1e4, 64, 0)
 
 
-def test_step_tokens():
-    assert pkv.step_tokens("f32") == 16
-    assert pkv.step_tokens("bf16") == 32
-    assert pkv.step_tokens("fp8") == 64
+def test_tile_tokens():
+    assert pkv.tile_tokens() == 16
 
 
 # ---- work partition ---------------------------------------------------------
-def reference_partition(lens, hkv, step, cap, n_waves, min_steps):
+def reference_partition(lens, hkv, cap, n_waves, min_tiles):
     """The partition written out plainly: sequences (b, h) in order, each cut
-    into max(1, ceil(min(L, cap)/step)) steps, then split evenly."""
-    ns = [max(1, -(-min(max(int(L), 0), cap) // step)) for L in lens]
+    into max(1, ceil(min(L, cap)/16)) tiles, then split evenly."""
+    ns = [max(1, -(-min(max(int(L), 0), cap) // 16)) for L in lens]
     seqs = [(b, h, ns[b]) for b in range(len(lens)) for h in range(hkv)]
     total = sum(n for _, _, n in seqs)
-    we = min(n_waves, max(1, -(-total // min_steps)))
+    we = min(n_waves, max(1, -(-total // min_tiles)))
     bounds = [(w * total) // we for w in range(we + 1)]
     owner = {}
     g = 0
     for b, h, n in seqs:
-        for st in range(n):
+        for t in range(n):
             w = max(i for i in range(we) if bounds[i] <= g)
-            owner[(b, h, st)] = w
+            owner[(b, h, t)] = w
             g += 1
     return owner, bounds, we, seqs
 
 
-@pytest.mark.parametrize("lens,hkv,step,waves,min_steps", [
-    ([138, 1012, 84], 4, 16, 64, 4),
-    ([1, 1, 1, 1], 2, 32, 64, 1),
-    ([5000, 3, 70, 31, 32, 33], 3, 32, 20, 2),
-    ([1], 1, 64, 8, 4),
-    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 32, 96, 3),
-    ([100] * 7, 2, 16, 1000, 1),          # more wavefronts than steps
-    ([0, -5, 40], 2, 32, 16, 1),          # invalid lengths still get one step
+@pytest.mark.parametrize("lens,hkv,waves,min_tiles", [
+    ([138, 1012, 84], 4, 64, 4),
+    ([1, 1, 1, 1], 2, 64, 1),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2),
+    ([1], 1, 8, 4),
+    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3),
+    ([100] * 7, 2, 1000, 1),          # more wavefronts than tiles
+    ([0, -5, 40], 2, 16, 1),          # invalid lengths still get one tile
+    ([16, 17, 15, 32, 33], 1, 5, 1),  # tile edges
 ])
-def test_partition_covers_every_step_once_and_balances(lens, hkv, step, waves, min_steps):
+def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_tiles):
     cap = 1 << 20
-    pieces, headers = pkv.plan_host(lens, hkv, step, cap, waves, min_steps)
-    owner, bounds, we, seqs = reference_partition(lens, hkv, step, cap, waves, min_steps)
+    pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_tiles)
+    owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_tiles)
     seen = {}
     per_wave = np.zeros(waves, dtype=np.int64)
-    for w, b, h, s0, s1, fl in pieces:
-        assert s0 < s1
-        for st in range(s0, s1):
-            assert (b, h, st) not in seen
-            seen[(b, h, st)] = w
-        per_wave[w] += s1 - s0
+    for w, b, h, t0, t1, fl in pieces:
+        assert t0 < t1
+        for t in range(t0, t1):
+            assert (b, h, t) not in seen
+            seen[(b, h, t)] = w
+        per_wave[w] += t1 - t0
     assert seen == owner
     active = per_wave[:we]
     assert active.min() >= 1 and active.max() - active.min() <= 1
     assert np.all(per_wave[we:] == 0)
-    # flags and reduce headers against a direct reading
+    # flags and split rows against a direct reading
     by_seq = {}
-    for w, b, h, s0, s1, fl in pieces:
-        by_seq.setdefault((b, h), []).append((w, s0, s1, fl))
-    trig = {}
+    for w, b, h, t0, t1, fl in pieces:
+        by_seq.setdefault((b, h), []).append((w, t0, t1, fl))
+    rows = {}
     for (b, h, n) in seqs:
         ps = by_seq[(b, h)]
         split = len(ps) > 1
-        for i, (w, s0, s1, fl) in enumerate(ps):
+        for i, (w, t0, t1, fl) in enumerate(ps):
             assert bool(fl & 1) == split
-            assert bool(fl & 4) == (s1 == n)
+            assert bool(fl & 4) == (t1 == n)
+            if split:   # only a wave's first or last piece can be split
+                first_of_wave = bool(fl & 2)
+                last_of_wave = w == ps[-1][0] or t1 < n
+                assert first_of_wave or last_of_wave
         if split:
-            w_last = ps[-1][0]
-            w_first = ps[0][0]
-            first_is_first_piece = bool(ps[0][3] & 2)
-            trig[w_last] = (b * hkv + h, w_first, (0 if first_is_first_piece else 1) | (len(ps) << 1))
+            w_first, w_last = ps[0][0], ps[-1][0]
             assert [p[0] for p in ps] == list(range(w_first, w_last + 1))
+            # partial slot of the first piece: 0 iff it is its wave's first piece
+            rows[w_first] = (b * hkv + h, len(ps), 0 if ps[0][3] & 2 else 1)
     for w in range(waves):
-        hdr = headers[w]
-        if w in trig:
-            assert hdr[0] == 1 and tuple(hdr[1:]) == trig[w]
+        row = splits[w]
+        if w in rows:
+            assert row[0] == 1 and tuple(row[1:]) == rows[w]
         else:
-            assert hdr[0] == 0
+            assert row[0] == 0

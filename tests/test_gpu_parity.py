@@ -59,9 +59,9 @@ def test_config_leading_requests(k, batch):
 
 # ---------------------------------------------------------------- edge cases
 def edge_lengths(kv, bs):
-    step = pkv.step_tokens(kv)
-    ls = {1, 2, 3, 5, bs - 1, bs, bs + 1, 2 * bs, step - 1, step, step + 1,
-          2 * step + 7, 3 * step, 300}
+    t = pkv.tile_tokens()
+    ls = {1, 2, 3, 4, 5, bs - 1, bs, bs + 1, 2 * bs, t - 1, t, t + 1,
+          2 * t + 7, 3 * t, 4 * t + 3, 300}
     return sorted(x for x in ls if x >= 1)
 
 
@@ -90,8 +90,8 @@ def test_nan_poison_in_unused_slots_blocks_and_table_tails(kv):
 def test_many_splits_and_no_split_agree(kv):
     wl = small([2000, 50, 3333, 1, 900], kv=kv, hq=32, hkv=8)
     arrs = problem.build(wl)
-    out_a, ref, _ = run_and_check(wl, arrs, waves_per_cu=16, min_steps=1)
-    out_b, _, _ = run_and_check(wl, arrs, waves_per_cu=4, min_steps=100000)
+    out_a, ref, _ = run_and_check(wl, arrs, waves_per_cu=16, min_tiles=1)
+    out_b, _, _ = run_and_check(wl, arrs, waves_per_cu=4, min_tiles=100000)
     err = gp.row_rel_err(out_a, out_b)
     assert err.max() <= gp.tolerance(kv)
 
