@@ -176,35 +176,45 @@ def cpu_baseline(wl, pool, tens, scales, budget_s: float):
     except Exception:  # threadpoolctl missing: numpy's default
         limiter, threads = None, len(os.sched_getaffinity(0))
     c = wl.cfg
-    elapsed, done_bytes, done_req = 0.0, 0, 0
-    order = list(range(wl.batch))
-    for b in order:
-        nblk = int(wl.n_blocks_used()[b])
-        ids = torch.from_numpy(wl.block_tables[b, :nblk].astype(np.int64)).to(pool.k_storage().device)
-        k, v = pool_io.gather_blocks_logical(pool, ids)
-        kc, vc = gp.codes_from_torch(k, c.kv_dtype), gp.codes_from_torch(v, c.kv_dtype)
-        mwl, arrs = gp.mini_problem(wl, b, kc, vc, io, scales)
-        t0 = time.perf_counter()
-        oracle.decode_step(k_pool=arrs["k_pool"], v_pool=arrs["v_pool"], kv_dtype=c.kv_dtype,
-                           io_dtype=c.io_dtype, q=arrs["q"], k_new=arrs["k_new"],
-                           v_new=arrs["v_new"], positions=mwl.positions,
-                           block_tables=mwl.block_tables, context_lens=mwl.context_lens,
-                           block_size=c.block_size, rope_theta=c.rope_theta,
-                           k_scale=arrs["k_scale"], v_scale=arrs["v_scale"])
-        elapsed += time.perf_counter() - t0
-        done_bytes += algorithmic_bytes(mwl)
-        done_req += 1
-        if elapsed >= budget_s:
-            break
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+    elapsed, done_bytes, done_req, passes = 0.0, 0, 0, 0
+    budget_hit = False
+    # whole passes over the workload's requests (or the leading requests of
+    # one pass) until the budget of CPU work is used
+    while not budget_hit and passes < 1000:
+        passes += 1
+        for b in range(wl.batch):
+            nblk = int(wl.n_blocks_used()[b])
+            ids = torch.from_numpy(wl.block_tables[b, :nblk].astype(np.int64)).to(
+                pool.k_storage().device)
+            k, v = pool_io.gather_blocks_logical(pool, ids)
+            kc, vc = gp.codes_from_torch(k, c.kv_dtype), gp.codes_from_torch(v, c.kv_dtype)
+            mwl, arrs = gp.mini_problem(wl, b, kc, vc, io, scales)
+            t0 = time.perf_counter()
+            oracle.decode_step(k_pool=arrs["k_pool"], v_pool=arrs["v_pool"], kv_dtype=c.kv_dtype,
+                               io_dtype=c.io_dtype, q=arrs["q"], k_new=arrs["k_new"],
+                               v_new=arrs["v_new"], positions=mwl.positions,
+                               block_tables=mwl.block_tables, context_lens=mwl.context_lens,
+                               block_size=c.block_size, rope_theta=c.rope_theta,
+                               k_scale=arrs["k_scale"], v_scale=arrs["v_scale"])
+            elapsed += time.perf_counter() - t0
+            done_bytes += algorithmic_bytes(mwl)
+            done_req += 1
+            if elapsed >= budget_s:
+                budget_hit = True
+                break
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    if passes == 1 and budget_hit:
+        sample = f"the first {done_req} of {wl.batch} requests of the workload"
+    else:
+        sample = (f"{done_req} requests: {passes} passes over all {wl.batch} requests of the "
+                  f"workload (the last one partial)")
     return {
         "value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s",
         "tokens_per_s_per_layer": round(done_req / elapsed, 2),
         "cores": int(threads), "kind": "oracle",
-        "sample": f"first {done_req} of {wl.batch} requests of the same workload "
-                  f"({elapsed:.1f} s of numpy fp64 work; block gather, RoPE, append, "
-                  f"attention; input transfer excluded)",
+        "sample": f"{sample}; {elapsed:.1f} s of numpy fp64 work (block gather, RoPE, append, "
+                  f"attention per request; device-to-host transfer excluded)",
     }
 
 
@@ -217,6 +227,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run --steps plain device copies of 1 GiB (for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
@@ -228,6 +241,15 @@ def main():
 
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}), flush=True)
+        return
     wl = workloads.make_workload(args.config)
     c = wl.cfg
     alg = algorithmic_bytes(wl)
@@ -247,8 +269,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, bracketed by synchronisation; events on the
-    # stream the kernels are launched on (torch's current stream)
+    # timed region: K steps, bracketed by synchronisation; the step events
+    # are on the stream the kernels are launched on (torch's current stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -260,8 +282,9 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # kernel durations from HIP events around each launch (a separate pass,
-    # so the events do not sit in the timed region above)
+    # the same K steps again, each kernel launched with start/stop events
+    # that its own dispatch stamps (kernel durations, for the roofline); a
+    # pass of its own so that the event packets do not sit in the timed steps
     for p in pools:
         p.enable_timing(True)
     for i in range(args.steps):

@@ -193,13 +193,13 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
                               int32_t min_tiles);
 
-/* Measurement.  While enabled, decode_step records HIP events on its launch
- * stream before the attention kernel, between it and the split-merge kernel,
- * and after the merge.  kv_pool_read_timing waits for the recorded events,
- * returns the summed milliseconds of each kind (event to event, so the merge
- * figure includes the gap between the two launches) and the number of
- * decode_step calls since the last read (or enable), and starts over.  At
- * most 65536 calls are recorded between reads (later ones are not timed). */
+/* Measurement.  While enabled, decode_step launches its two kernels (the
+ * fused attention kernel and the split-merge kernel) with HIP start/stop
+ * events that the dispatches themselves stamp.  kv_pool_read_timing waits
+ * for the recorded events, returns the summed kernel milliseconds of each
+ * kind and the number of decode_step calls since the last read (or enable),
+ * and starts over.  At most 65536 calls are recorded between reads (later
+ * ones are not timed). */
 pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable);
 pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms,
                                int32_t* calls);

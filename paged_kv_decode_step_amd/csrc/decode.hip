@@ -52,6 +52,8 @@
 // second launch: the kernel boundary makes them visible across the eight
 // XCDs' L2 caches with one write-back, where a device-scope release inside
 // the kernel would write back an XCD's whole L2 once per wavefront.
+#include <hip/hip_ext.h>
+
 #include <utility>
 
 #include "kernels.h"
@@ -892,18 +894,18 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
 
 template <int KV, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
-  hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_attn_kernel<KV, D, BS>), dim3(p.n_waves / 4), dim3(kBlockThreads),
-                     0, stream, p, p.block_tables, p.context_lens, p.positions,
-                     static_cast<char*>(p.k_pool), static_cast<char*>(p.v_pool));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<KV != KV_F32, D>), dim3(p.n_waves / 4),
-                     dim3(kBlockThreads), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-  return hipSuccess;
+  // With events, the start/stop stamps are taken by the dispatch packets of
+  // the kernels themselves (ev[0..1] attention, ev[2..3] merge).
+  hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS>), dim3(p.n_waves / 4), dim3(kBlockThreads),
+                        0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, p,
+                        p.block_tables, p.context_lens, p.positions,
+                        static_cast<char*>(p.k_pool), static_cast<char*>(p.v_pool));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipExtLaunchKernelGGL((decode_merge_kernel<KV != KV_F32, D>), dim3(p.n_waves / 4),
+                        dim3(kBlockThreads), 0, stream, ev ? ev[2] : nullptr,
+                        ev ? ev[3] : nullptr, 0, p);
+  return hipGetLastError();
 }
 
 template <int KV, int D, int BS>

@@ -48,7 +48,7 @@ struct DecodeParams {
 constexpr int partial_floats(int head_dim) { return 16 * head_dim + 2 * kGroupMax; }
 
 // Launch the fused append+attention kernel and the split-merge kernel on
-// `stream`, with `events` (3 of them) recorded before, between and after.
+// `stream`; with `events` (4 of them), the start and stop of each kernel.
 hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
                          hipStream_t stream, hipEvent_t* events);
 

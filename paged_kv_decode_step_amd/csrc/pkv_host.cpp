@@ -78,7 +78,7 @@ struct pkv_pool {
   int waves_per_cu = 0;
   int n_waves = 0;
   int min_tiles = 16;
-  // measurement: event triplets (before attention, between, after merge)
+  // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
   int timed_calls = 0;
@@ -440,14 +440,14 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
-    const size_t need = 3 * (size_t)(pool->timed_calls + 1);
+    const size_t need = 4 * (size_t)(pool->timed_calls + 1);
     while (pool->events.size() < need) {
       hipEvent_t e;
       hipError_t he = hipEventCreate(&e);
       if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
       pool->events.push_back(e);
     }
-    ev = &pool->events[3 * (size_t)pool->timed_calls];
+    ev = &pool->events[4 * (size_t)pool->timed_calls];
     ++pool->timed_calls;
   }
   hipError_t e = pkv::launch_decode(kv_kind(pool->kv_dtype), pool->head_dim, pool->block_size, p,
@@ -468,12 +468,12 @@ pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms
   if (!pool || !attn_ms || !merge_ms || !calls) return fail(PKV_ERR_INVALID, "null argument");
   double a = 0.0, m = 0.0;
   for (int i = 0; i < pool->timed_calls; ++i) {
-    hipEvent_t* ev = &pool->events[3 * (size_t)i];
-    hipError_t e = hipEventSynchronize(ev[2]);
+    hipEvent_t* ev = &pool->events[4 * (size_t)i];
+    hipError_t e = hipEventSynchronize(ev[3]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     float t0 = 0.f, t1 = 0.f;
     e = hipEventElapsedTime(&t0, ev[0], ev[1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&t1, ev[1], ev[2]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, ev[2], ev[3]);
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     a += t0;
     m += t1;
