@@ -101,6 +101,9 @@ typedef struct pkv_pool_info {
   int32_t device;            /* HIP device ordinal */
   int32_t n_waves;           /* wavefronts one decode_step launch runs */
   int64_t workspace_bytes;
+  int32_t ring_tiles;        /* tiles each wavefront keeps in flight */
+  int32_t min_units;         /* tuning in effect (kv_pool_set_tuning) */
+  int32_t piece_cost;
 } pkv_pool_info;
 
 /* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
@@ -185,13 +188,20 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
  * context length outside [1, max_blocks_per_seq * block_size]. */
 pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 
-/* Tuning knobs (also read from PKV_WAVES_PER_CU and PKV_MIN_TILES at pool
- * creation).  waves_per_cu: wavefronts per compute unit the step is spread
- * over (0 = as many as are resident at once, 8 on gfx950); min_tiles: fewest
- * 16-token tiles a wavefront is given before fewer wavefronts are used
- * (>= 1; default 16).  Synchronises the device. */
+/* Tuning knobs (also read from PKV_WAVES_PER_CU, PKV_MIN_UNITS and
+ * PKV_PIECE_COST at pool creation).  The step's work is measured in units:
+ * one per 16-token tile, plus piece_cost for starting each (request, KV
+ * head) sequence (its query rotation and append stall the wavefront's
+ * loads), and split evenly over the wavefronts.  waves_per_cu: wavefronts
+ * per compute unit (0 = as many as are resident at once, 8 on gfx950);
+ * min_units: fewest units a wavefront is given before fewer wavefronts are
+ * used (>= 1; raised to piece_cost + 1; default 16); piece_cost in [0, 64],
+ * or -1 (the default) for ring_tiles + 2: a sequence start waits for the
+ * wavefront's whole ring of in-flight tile loads (about ring_tiles
+ * tile-times at full bandwidth) and then for its own query loads.
+ * Synchronises the device. */
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
-                              int32_t min_tiles);
+                              int32_t min_units, int32_t piece_cost);
 
 /* Measurement.  While enabled, decode_step launches its two kernels (the
  * fused attention kernel and the split-merge kernel) with HIP start/stop
@@ -228,21 +238,24 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
                                float* sin_out);
 
 /* The work partition decode_step's kernel computes on the device, replayed
- * on the host from host copies of context_lens, for testing.  The batch's
- * (request, KV head) sequences, each cut into 16-token tiles (at least one;
- * lengths clamped to [0, max_tokens]), are concatenated and split evenly over
- * min(n_waves, ceil(N / min_tiles)) wavefronts.  Writes up to max_pieces rows
- * of 6 int32 to pieces: {wave, request, kv_head, first_tile, end_tile, flags}
- * with flags bit 0 = the piece is part of a split sequence, bit 1 = it is the
- * wave's first piece, bit 2 = it is the last piece of its sequence; and
- * n_waves rows of 4 int32 to splits: row w describes the split sequence whose
- * first piece wave w holds, {1, request * n_kv_heads + kv_head, pieces,
- * partial slot of the first piece}, or zeros.  *n_pieces receives the total
- * count. */
+ * on the host from host copies of context_lens, for testing.  Each
+ * (request, KV head) sequence is cut into 16-token tiles (at least one;
+ * lengths clamped to [0, max_tokens]) and costs its tiles plus piece_cost
+ * units; its tile 0 owns the units [s, s + piece_cost], tile j >= 1 the unit
+ * s + piece_cost + j.  The sequences' units are concatenated in (request,
+ * head) order and split evenly over min(n_waves, ceil(C / max(min_units,
+ * piece_cost + 1))) wavefronts; a wavefront takes the tiles whose first unit
+ * falls in its range.  Writes up to max_pieces rows of 6 int32 to pieces:
+ * {wave, request, kv_head, first_tile, end_tile, flags} with flags bit 0 =
+ * the piece is part of a split sequence, bit 1 = it is the wave's first
+ * piece, bit 2 = it is the last piece of its sequence; and n_waves rows of
+ * 4 int32 to splits: row w describes the split sequence whose first piece
+ * wave w holds, {1, request * n_kv_heads + kv_head, pieces, partial slot of
+ * the first piece}, or zeros.  *n_pieces receives the total count. */
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
                          int32_t n_kv_heads, int32_t max_tokens, int32_t n_waves,
-                         int32_t min_tiles, int32_t max_pieces, int32_t* pieces,
-                         int32_t* n_pieces, int32_t* splits);
+                         int32_t min_units, int32_t piece_cost, int32_t max_pieces,
+                         int32_t* pieces, int32_t* n_pieces, int32_t* splits);
 
 /* Tokens per tile, the kernel's unit of work (16). */
 int32_t pkv_tile_tokens(void);

@@ -67,6 +67,11 @@
 #ifndef PKV_RING_BYTES_FP8
 #define PKV_RING_BYTES_FP8 24576
 #endif
+// Resident wavefronts per SIMD the attention kernel is compiled for (its
+// register budget is 512 / this).
+#ifndef PKV_WAVES_PER_EU
+#define PKV_WAVES_PER_EU 2
+#endif
 
 namespace pkv {
 namespace {
@@ -282,19 +287,20 @@ struct Walk {
   int b, h, j, n;   // request, KV head, tile in the sequence, tiles of the sequence
 };
 
-__device__ __forceinline__ void walk_next(Walk& w, const int* sP, int B, int hkv) {
+__device__ __forceinline__ void walk_next(Walk& w, const int* sP, int B, int hkv, int cost) {
   if (++w.j == w.n) {
     w.j = 0;
     if (++w.h == hkv) {
       w.h = 0;
-      if (++w.b < B) w.n = uniform(sP[w.b + 1] - sP[w.b]);
+      if (++w.b < B) w.n = uniform(tiles_per_seq(sP, w.b, hkv, cost));
     }
   }
 }
 
 // ---------------------------------------------------------------- kernel
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBlockThreads)
+__attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU, PKV_WAVES_PER_EU)))
 void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
                         const int32_t* __restrict__ lens, const int32_t* __restrict__ poss,
                         char* __restrict__ kpool, char* __restrict__ vpool) {
@@ -313,8 +319,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int B = p.batch, hkv = p.n_kv_heads, G = p.group;
   const int cap = p.max_blocks * BS;
 
-  // ---- tiles per request, prefix-summed into LDS (every workgroup)
-  for (int i = tid; i < B; i += kBlockThreads) sP[i] = tiles_of(lens[i], cap);
+  const int cost = p.piece_cost;
+  // ---- work units per request (hkv sequences of tiles + cost each),
+  // prefix-summed into LDS (every workgroup)
+  for (int i = tid; i < B; i += kBlockThreads) sP[i] = hkv * (tiles_of(lens[i], cap) + cost);
   __syncthreads();
   {
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
@@ -343,25 +351,42 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     __syncthreads();
   }
 
-  const int64_t N = (int64_t)hkv * sP[B];
-  const int64_t W = active_waves(N, p.n_waves, p.min_tiles);
+  const int64_t U = sP[B];                               // work units
+  const int64_t W = active_waves(U, p.n_waves, p.min_units);
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
   if (wave >= W) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
     return;
   }
-  const int64_t start = wave_start(wave, N, W);
-  const int T = uniform((int)(wave_start(wave + 1, N, W) - start));
-
+  // The wave's tiles: those whose first unit lies in its unit range.
   Walk w0;
+  int T;
   {
-    const int b = uniform(find_request(sP, B, start, hkv));
-    const int n = uniform(sP[b + 1] - sP[b]);
-    const int r = (int)(start - (int64_t)hkv * sP[b]);
-    w0.b = b;
-    w0.h = r / n;
-    w0.j = r - w0.h * n;
-    w0.n = n;
+    const TilePos t0 = tile_at_unit(sP, B, hkv, cost, wave_start(wave, U, W));
+    const int64_t g0 = global_tile(sP, t0.b, t0.h, t0.j, t0.n, hkv, cost);
+    const int64_t x1 = wave_start(wave + 1, U, W);
+    int64_t g1 = (int64_t)sP[B] - (int64_t)hkv * cost * B;       // all tiles
+    if (x1 < U) {
+      const TilePos t1 = tile_at_unit(sP, B, hkv, cost, x1);
+      g1 = global_tile(sP, t1.b, t1.h, t1.j, t1.n, hkv, cost);
+    }
+    T = uniform((int)(g1 - g0));
+    w0.b = uniform(t0.b);
+    w0.h = uniform(t0.h);
+    w0.j = uniform(t0.j);
+    w0.n = uniform(t0.n);
+    if (T > 0 && w0.j == w0.n) {        // the range begins at the next sequence
+      w0.j = 0;
+      if (++w0.h == hkv) {
+        w0.h = 0;
+        ++w0.b;
+        w0.n = uniform(tiles_per_seq(sP, w0.b, hkv, cost));
+      }
+    }
+  }
+  if (T <= 0) {
+    if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
+    return;
   }
 
   const int lane16 = lane * 16;
@@ -400,7 +425,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     if (pf_live) {
       --p_left;
       if (p_left > 0) {
-        walk_next(pw, sP, B, hkv);
+        walk_next(pw, sP, B, hkv, cost);
         pf_blk = load_blk(pw);
       }
     }
@@ -780,8 +805,8 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       }
     }
     if (j0 == 0) {
-      const int64_t sb = (int64_t)hkv * sP[cw.b] + (int64_t)cw.h * cw.n;
-      const int np = (int)(wave_of_tile(sb + cw.n - 1, N, W) - wave + 1);
+      const int64_t last = first_unit(sP, cw.b, cw.h, cw.n - 1, cw.n, cost);
+      const int np = (int)(wave_of_unit(last, U, W) - wave + 1);
       split_hdr = make_int4(1, cw.b * hkv + cw.h, np, slot);
     }
   };
@@ -804,7 +829,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       issue_v(ring[u]);
       if (live) {
         if (i == T - 1 || last) end_piece();
-        walk_next(cw, sP, B, hkv);
+        walk_next(cw, sP, B, hkv, cost);
       }
     }, std::make_integer_sequence<int, R>{});
   }
@@ -943,6 +968,18 @@ hipError_t dispatch(int kv_kind, int head_dim, int bs, const DecodeParams* p, hi
 hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
                          hipStream_t stream, hipEvent_t* events) {
   return dispatch(kv_kind, head_dim, block_size, &p, stream, events, nullptr);
+}
+
+int decode_ring_tiles(int kv_kind, int head_dim) {
+  switch (kv_kind * 1000 + head_dim) {
+    case KV_F32 * 1000 + 64:   return Cfg<KV_F32, 64, 16>::RING;
+    case KV_F32 * 1000 + 128:  return Cfg<KV_F32, 128, 16>::RING;
+    case KV_BF16 * 1000 + 64:  return Cfg<KV_BF16, 64, 16>::RING;
+    case KV_BF16 * 1000 + 128: return Cfg<KV_BF16, 128, 16>::RING;
+    case KV_FP8 * 1000 + 64:   return Cfg<KV_FP8, 64, 16>::RING;
+    case KV_FP8 * 1000 + 128:  return Cfg<KV_FP8, 128, 16>::RING;
+    default: return 0;
+  }
 }
 
 hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks) {

@@ -11,6 +11,7 @@ constexpr int kMaxBatch = 4096;    // requests per step (LDS prefix array)
 constexpr int kWaveThreads = 64;
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
 constexpr int kTileTokens = 16;    // tokens per KV tile (the unit of work)
+constexpr int kMaxPieceCost = 64;  // work units a sequence start may cost
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -39,7 +40,8 @@ struct DecodeParams {
   int32_t max_blocks;        // block-table row length
   int32_t max_pos;
   int32_t n_waves;           // wavefronts launched (multiple of 4)
-  int32_t min_tiles;         // fewest tiles a wavefront is given
+  int32_t min_units;         // fewest work units a wavefront is given (> piece_cost)
+  int32_t piece_cost;        // work units a sequence costs on top of its tiles
   float sm_scale_log2;       // log2(e) / sqrt(D)
 };
 
@@ -51,6 +53,9 @@ constexpr int partial_floats(int head_dim) { return 16 * head_dim + 2 * kGroupMa
 // `stream`; with `events` (4 of them), the start and stop of each kernel.
 hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
                          hipStream_t stream, hipEvent_t* events);
+
+// Tiles the attention kernel keeps in flight per wavefront (its load ring).
+int decode_ring_tiles(int kv_kind, int head_dim);
 
 // Resident 256-thread workgroups per compute unit for the attention kernel.
 hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks_per_cu);

@@ -52,6 +52,15 @@ int env_int(const char* name, int dflt) {
   return std::atoi(s);
 }
 
+// Work units charged for starting a sequence.  Its query loads queue behind
+// every tile load the wavefront has in flight, so a start stalls the
+// wavefront for about its ring of tiles plus one more round trip (the query
+// and the append); -1 asks for that estimate, ring + 2.
+int resolve_piece_cost(int requested, int ring_tiles) {
+  const int c = requested < 0 ? ring_tiles + 2 : requested;
+  return std::max(0, std::min(c, pkv::kMaxPieceCost));
+}
+
 }  // namespace
 
 struct pkv_pool {
@@ -77,7 +86,9 @@ struct pkv_pool {
   int occ_blocks = 0;              // resident workgroups per CU (occupancy)
   int waves_per_cu = 0;
   int n_waves = 0;
-  int min_tiles = 16;
+  int min_units = 16;
+  int piece_cost = 0;       // resolved (never the automatic -1)
+  int ring_tiles = 0;
   // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -195,7 +206,9 @@ pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_h
   e = pkv::decode_occupancy(kv_kind(kv_dtype), head_dim, block_size, &p->occ_blocks);
   if (e != hipSuccess) { free_pool(p); return hip_fail(e, "occupancy query"); }
   p->occ_blocks = std::max(1, p->occ_blocks);
-  p->min_tiles = std::max(1, env_int("PKV_MIN_TILES", 16));
+  p->min_units = std::max(1, env_int("PKV_MIN_UNITS", 16));
+  p->ring_tiles = pkv::decode_ring_tiles(kv_kind(kv_dtype), head_dim);
+  p->piece_cost = resolve_piece_cost(env_int("PKV_PIECE_COST", -1), p->ring_tiles);
   pkv_status s = size_workspace(p, env_int("PKV_WAVES_PER_CU", 0));
   if (s != PKV_OK) { free_pool(p); return s; }
   *out_pool = p;
@@ -282,12 +295,19 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->device = pool->device;
   info->n_waves = pool->n_waves;
   info->workspace_bytes = pool->ws_bytes;
+  info->ring_tiles = pool->ring_tiles;
+  info->min_units = pool->min_units;
+  info->piece_cost = pool->piece_cost;
   return PKV_OK;
 }
 
-pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_tiles) {
+pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_units,
+                              int32_t piece_cost) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
-  if (min_tiles < 1) return fail(PKV_ERR_INVALID, "min_tiles must be >= 1");
+  if (min_units < 1) return fail(PKV_ERR_INVALID, "min_units must be >= 1");
+  if (piece_cost < -1 || piece_cost > pkv::kMaxPieceCost)
+    return fail(PKV_ERR_INVALID, "piece_cost must be -1 (automatic) or in [0, %d]",
+                pkv::kMaxPieceCost);
   if (waves_per_cu < 0 || waves_per_cu > 32)
     return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
   int cur = 0;
@@ -297,7 +317,8 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
   pkv_status s = size_workspace(pool, waves_per_cu);
   (void)hipSetDevice(cur);
   if (s != PKV_OK) return s;
-  pool->min_tiles = min_tiles;
+  pool->min_units = min_units;
+  pool->piece_cost = resolve_piece_cost(piece_cost, pool->ring_tiles);
   return PKV_OK;
 }
 
@@ -335,8 +356,9 @@ pkv_status pkv_check_decode_args(int64_t num_blocks, int32_t block_size, int32_t
   if (cap > ((int64_t)1 << 24))
     return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq * block_size above 2^24 tokens");
   const int64_t tile = pkv::kTileTokens;
-  if ((int64_t)batch * n_kv_heads * ((cap + tile - 1) / tile) > ((int64_t)1 << 31) - 1)
-    return fail(PKV_ERR_UNSUPPORTED, "batch * n_kv_heads * tiles above 2^31");
+  if ((int64_t)batch * n_kv_heads * ((cap + tile - 1) / tile + pkv::kMaxPieceCost) >
+      ((int64_t)1 << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "batch * n_kv_heads * (tiles + piece cost) above 2^31");
   if (batch == 0) return PKV_OK;
   if (!q || !k_new || !v_new || !positions || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_INVALID, "null device pointer");
@@ -436,7 +458,8 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.max_blocks = max_blocks_per_seq;
   p.max_pos = pool->rope_max_pos;
   p.n_waves = pool->n_waves;
-  p.min_tiles = pool->min_tiles;
+  p.piece_cost = pool->piece_cost;
+  p.min_units = std::max(pool->min_units, pool->piece_cost + 1);
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
@@ -497,59 +520,78 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
 }
 
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
-                         int32_t max_tokens, int32_t n_waves, int32_t min_tiles,
-                         int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
-                         int32_t* splits) {
+                         int32_t max_tokens, int32_t n_waves, int32_t min_units,
+                         int32_t piece_cost, int32_t max_pieces, int32_t* pieces,
+                         int32_t* n_pieces, int32_t* splits) {
   if (!context_lens || !n_pieces || !splits || (max_pieces > 0 && !pieces))
     return fail(PKV_ERR_INVALID, "null argument");
-  if (batch < 1 || n_kv_heads < 1 || n_waves < 1 || min_tiles < 1 || max_tokens < 1)
+  if (batch < 1 || n_kv_heads < 1 || n_waves < 1 || min_units < 1 || max_tokens < 1)
     return fail(PKV_ERR_INVALID, "sizes must be positive");
+  if (piece_cost < 0 || piece_cost > pkv::kMaxPieceCost)
+    return fail(PKV_ERR_INVALID, "piece_cost must be in [0, %d]", pkv::kMaxPieceCost);
+  const int hkv = n_kv_heads, cost = piece_cost;
   std::vector<int> P(batch + 1, 0);
-  for (int b = 0; b < batch; ++b) P[b + 1] = P[b] + pkv::tiles_of(context_lens[b], max_tokens);
-  const int64_t N = (int64_t)n_kv_heads * P[batch];
-  const int64_t W = pkv::active_waves(N, n_waves, min_tiles);
+  for (int b = 0; b < batch; ++b)
+    P[b + 1] = P[b] + hkv * (pkv::tiles_of(context_lens[b], max_tokens) + cost);
+  const int64_t C = P[batch];
+  const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1));
+  const int64_t n_tiles = (int64_t)P[batch] - (int64_t)hkv * cost * batch;
   for (int64_t w = 0; w < n_waves; ++w) {
     int32_t* row = splits + 4 * w;
     row[0] = row[1] = row[2] = row[3] = 0;
   }
   int64_t count = 0;
   for (int64_t w = 0; w < W; ++w) {
-    const int64_t start = pkv::wave_start(w, N, W), end = pkv::wave_start(w + 1, N, W);
-    int b = pkv::find_request(P.data(), batch, start, n_kv_heads);
-    int n = P[b + 1] - P[b];
-    int64_t rbase = (int64_t)n_kv_heads * P[b];
-    int h = (int)((start - rbase) / n);
-    int64_t pos = start;
+    pkv::TilePos t = pkv::tile_at_unit(P.data(), batch, hkv, cost, pkv::wave_start(w, C, W));
+    const int64_t g0 = pkv::global_tile(P.data(), t.b, t.h, t.j, t.n, hkv, cost);
+    int64_t g1 = n_tiles;
+    const int64_t x1 = pkv::wave_start(w + 1, C, W);
+    if (x1 < C) {
+      const pkv::TilePos t1 = pkv::tile_at_unit(P.data(), batch, hkv, cost, x1);
+      g1 = pkv::global_tile(P.data(), t1.b, t1.h, t1.j, t1.n, hkv, cost);
+    }
+    int64_t left = g1 - g0;
+    if (left > 0 && t.j == t.n) {
+      t.j = 0;
+      if (++t.h == hkv) {
+        t.h = 0;
+        ++t.b;
+        t.n = pkv::tiles_per_seq(P.data(), t.b, hkv, cost);
+      }
+    }
     bool first = true;
-    while (pos < end) {
-      const int64_t sb = rbase + (int64_t)h * n, se = sb + n;
-      const int64_t pe = se < end ? se : end;
-      const bool split = sb < start || se > end;
+    while (left > 0) {
+      const int j0 = t.j;
+      const int64_t take = std::min<int64_t>(left, t.n - j0);
+      const int pe = j0 + (int)take;
+      const bool split = j0 > 0 || pe < t.n;
       if (count < max_pieces) {
         int32_t* r = pieces + 6 * count;
         r[0] = (int32_t)w;
-        r[1] = b;
-        r[2] = h;
-        r[3] = (int32_t)(pos - sb);
-        r[4] = (int32_t)(pe - sb);
+        r[1] = t.b;
+        r[2] = t.h;
+        r[3] = j0;
+        r[4] = pe;
         r[5] = (split ? pkv::PIECE_SPLIT : 0) | (first ? pkv::PIECE_FIRST : 0) |
-               (pe == se ? pkv::PIECE_LAST : 0);
+               (pe == t.n ? pkv::PIECE_LAST : 0);
       }
       ++count;
-      if (split && sb >= start) {       // the sequence starts here: wave w is its first
+      if (split && j0 == 0) {     // the sequence starts here: wave w is its first
         int32_t* row = splits + 4 * w;
+        const int64_t last = pkv::first_unit(P.data(), t.b, t.h, t.n - 1, t.n, cost);
         row[0] = 1;
-        row[1] = b * n_kv_heads + h;
-        row[2] = (int32_t)(pkv::wave_of_tile(se - 1, N, W) - w + 1);
-        row[3] = pkv::first_piece_slot(sb, w, N, W);
+        row[1] = t.b * hkv + t.h;
+        row[2] = (int32_t)(pkv::wave_of_unit(last, C, W) - w + 1);
+        row[3] = first ? 0 : 1;
       }
       first = false;
-      pos = pe;
-      if (++h == n_kv_heads) {
-        h = 0;
-        if (++b < batch) {
-          n = P[b + 1] - P[b];
-          rbase = (int64_t)n_kv_heads * P[b];
+      left -= take;
+      t.j = pe;
+      if (t.j == t.n) {
+        t.j = 0;
+        if (++t.h == hkv) {
+          t.h = 0;
+          if (++t.b < batch) t.n = pkv::tiles_per_seq(P.data(), t.b, hkv, cost);
         }
       }
     }

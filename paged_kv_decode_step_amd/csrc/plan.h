@@ -10,17 +10,21 @@
 //
 //  * a sequence is one (request b, KV head h) pair; it is cut into tiles of
 //    16 tokens (the last one partial), at least one tile each;
-//  * sequences are concatenated in (b, h) order: N tiles in all;
-//  * wavefront w of W active ones takes tiles [w*N/W, (w+1)*N/W), so any two
-//    wavefronts differ by at most one tile whatever the length mix;
+//  * a sequence of n tiles costs n + A work units: one per tile, plus A for
+//    starting it (the query rotation and, at its end, the append; a
+//    wavefront pays these with its loads stalled), and its first tile owns
+//    the A + 1 units [s, s + A], tile j >= 1 the unit s + A + j;
+//  * sequences are concatenated in (b, h) order: C units in all;
+//  * wavefront w of W active ones takes the units [w*C/W, (w+1)*C/W), i.e.
+//    the tiles whose first unit falls there, so wavefronts that start many
+//    short sequences get fewer tiles and all of them finish together;
 //  * a sequence cut between wavefronts ("split") leaves one partial softmax
-//    state per piece; the wavefront that finishes the last of its pieces
-//    merges them.
+//    state per piece; a second kernel merges them.
 //
 // A split sequence starts in exactly one wavefront (as that wavefront's last
-// piece), so the arrival counter and the merge of a split sequence are keyed
-// by that first wavefront.  A wavefront keeps at most two partial states:
-// slot 0 for its first piece, slot 1 for its last piece.
+// piece) and its pieces sit in consecutive wavefronts (every wavefront owns
+// at least one tile when W <= C / (A + 1)).  A wavefront keeps at most two
+// partial states: slot 0 for its first piece, slot 1 for its last piece.
 #pragma once
 
 #include <stdint.h>
@@ -49,43 +53,66 @@ PKV_HD inline int tiles_of(int L, int cap) {
   return n < 1 ? 1 : n;
 }
 
-// Active wavefronts: all of them, unless that leaves fewer than min_tiles
-// tiles each.  Never more than N, so every active wavefront has work.
-PKV_HD inline int64_t active_waves(int64_t n_tiles, int64_t n_waves, int64_t min_tiles) {
-  int64_t by_min = (n_tiles + min_tiles - 1) / min_tiles;
+// Active wavefronts: all of them, unless that leaves fewer than min_units
+// work units each.  Never more than C, so every active wavefront has work.
+PKV_HD inline int64_t active_waves(int64_t n_units, int64_t n_waves, int64_t min_units) {
+  int64_t by_min = (n_units + min_units - 1) / min_units;
   if (by_min < 1) by_min = 1;
   return n_waves < by_min ? n_waves : by_min;
 }
 
-PKV_HD inline int64_t wave_start(int64_t w, int64_t n_tiles, int64_t n_active) {
-  return (w * n_tiles) / n_active;
+PKV_HD inline int64_t wave_start(int64_t w, int64_t n_units, int64_t n_active) {
+  return (w * n_units) / n_active;
 }
 
-// The wavefront whose range holds global tile g: the largest w with
-// wave_start(w) <= g.
-PKV_HD inline int64_t wave_of_tile(int64_t g, int64_t n_tiles, int64_t n_active) {
-  return ((g + 1) * n_active - 1) / n_tiles;
+// The wavefront whose unit range holds unit u: the largest w with
+// wave_start(w) <= u.
+PKV_HD inline int64_t wave_of_unit(int64_t u, int64_t n_units, int64_t n_active) {
+  return ((u + 1) * n_active - 1) / n_units;
 }
 
-// Largest b in [0, B) with hkv * P[b] <= pos, for a strictly increasing
-// prefix array P (P[0] = 0) of tiles per request.
-PKV_HD inline int find_request(const int* P, int B, int64_t pos, int hkv) {
+// Largest b in [0, B) with P[b] <= pos, for a non-decreasing prefix array
+// P (P[0] = 0) of work units per request (P[b + 1] > P[b]).
+PKV_HD inline int find_request(const int* P, int B, int64_t pos) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)hkv * P[mid] <= pos) lo = mid; else hi = mid - 1;
+    if ((int64_t)P[mid] <= pos) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
 
-// Where the partial state of a split sequence's piece k lives, given the
-// sequence's first global tile `seq_begin` and first wavefront wf: piece k
-// is held by wavefront wf + k; pieces k > 0 are their wavefront's first
-// piece (slot 0); piece 0 is wavefront wf's last piece, which is also its
-// first (slot 0) only if wf starts exactly at the sequence.
-PKV_HD inline int first_piece_slot(int64_t seq_begin, int64_t wf, int64_t n_tiles,
-                                   int64_t n_active) {
-  return wave_start(wf, n_tiles, n_active) == seq_begin ? 0 : 1;
+// Units of request b (hkv sequences of n tiles) and its tiles per sequence,
+// from the unit prefix array.
+PKV_HD inline int tiles_per_seq(const int* P, int b, int hkv, int cost) {
+  return (P[b + 1] - P[b]) / hkv - cost;
+}
+
+// First unit of tile j of sequence (b, h) with n tiles.
+PKV_HD inline int64_t first_unit(const int* P, int b, int h, int j, int n, int cost) {
+  return (int64_t)P[b] + (int64_t)h * (n + cost) + (j == 0 ? 0 : cost + j);
+}
+
+// The first tile whose first unit is >= x (x < total units), as
+// (request, head, tile), with the tile possibly == n (then it is tile 0 of
+// the next sequence).
+struct TilePos { int b, h, j, n; };
+PKV_HD inline TilePos tile_at_unit(const int* P, int B, int hkv, int cost, int64_t x) {
+  TilePos t;
+  t.b = find_request(P, B, x);
+  t.n = tiles_per_seq(P, t.b, hkv, cost);
+  const int64_t r = x - P[t.b];
+  const int per = t.n + cost;
+  t.h = (int)(r / per);
+  const int c = (int)(r - (int64_t)t.h * per);
+  t.j = c == 0 ? 0 : (c - cost > 1 ? c - cost : 1);
+  return t;
+}
+
+// Global tile index (tiles of all sequences concatenated) of tile (b, h, j)
+// of a sequence with n tiles.
+PKV_HD inline int64_t global_tile(const int* P, int b, int h, int j, int n, int hkv, int cost) {
+  return ((int64_t)P[b] - (int64_t)hkv * cost * b) + (int64_t)h * n + j;
 }
 
 }  // namespace pkv

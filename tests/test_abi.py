@@ -100,38 +100,46 @@ def test_tile_tokens():
 
 
 # ---- work partition ---------------------------------------------------------
-def reference_partition(lens, hkv, cap, n_waves, min_tiles):
+def reference_partition(lens, hkv, cap, n_waves, min_units, cost):
     """The partition written out plainly: sequences (b, h) in order, each cut
-    into max(1, ceil(min(L, cap)/16)) tiles, then split evenly."""
+    into max(1, ceil(min(L, cap)/16)) tiles and costing its tiles plus
+    `cost` units (tile 0 owns cost + 1 units), the units split evenly and
+    each tile owned by the wave holding its first unit."""
     ns = [max(1, -(-min(max(int(L), 0), cap) // 16)) for L in lens]
     seqs = [(b, h, ns[b]) for b in range(len(lens)) for h in range(hkv)]
-    total = sum(n for _, _, n in seqs)
-    we = min(n_waves, max(1, -(-total // min_tiles)))
-    bounds = [(w * total) // we for w in range(we + 1)]
-    owner = {}
-    g = 0
+    first_units = []
+    u = 0
     for b, h, n in seqs:
         for t in range(n):
-            w = max(i for i in range(we) if bounds[i] <= g)
-            owner[(b, h, t)] = w
-            g += 1
+            first_units.append(((b, h, t), u))
+            u += cost + 1 if t == 0 else 1
+    total = u
+    we = min(n_waves, max(1, -(-total // max(min_units, cost + 1))))
+    bounds = [(w * total) // we for w in range(we + 1)]
+    owner = {}
+    for key, fu in first_units:
+        owner[key] = max(i for i in range(we) if bounds[i] <= fu)
     return owner, bounds, we, seqs
 
 
-@pytest.mark.parametrize("lens,hkv,waves,min_tiles", [
-    ([138, 1012, 84], 4, 64, 4),
-    ([1, 1, 1, 1], 2, 64, 1),
-    ([5000, 3, 70, 31, 32, 33], 3, 20, 2),
-    ([1], 1, 8, 4),
-    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3),
-    ([100] * 7, 2, 1000, 1),          # more wavefronts than tiles
-    ([0, -5, 40], 2, 16, 1),          # invalid lengths still get one tile
-    ([16, 17, 15, 32, 33], 1, 5, 1),  # tile edges
+@pytest.mark.parametrize("lens,hkv,waves,min_units,cost", [
+    ([138, 1012, 84], 4, 64, 4, 0),
+    ([138, 1012, 84], 4, 64, 4, 3),
+    ([1, 1, 1, 1], 2, 64, 1, 0),
+    ([1, 1, 1, 1], 2, 64, 1, 2),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 0),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 5),
+    ([1], 1, 8, 4, 3),
+    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3, 3),
+    (list(np.random.default_rng(1).integers(1, 200, 60)), 4, 200, 1, 7),
+    ([100] * 7, 2, 1000, 1, 1),       # more wavefronts than units allow
+    ([0, -5, 40], 2, 16, 1, 2),       # invalid lengths still get one tile
+    ([16, 17, 15, 32, 33], 1, 5, 1, 0),
 ])
-def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_tiles):
+def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_units, cost):
     cap = 1 << 20
-    pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_tiles)
-    owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_tiles)
+    pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_units, cost)
+    owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_units, cost)
     seen = {}
     per_wave = np.zeros(waves, dtype=np.int64)
     for w, b, h, t0, t1, fl in pieces:
@@ -141,9 +149,10 @@ def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_til
             seen[(b, h, t)] = w
         per_wave[w] += t1 - t0
     assert seen == owner
-    active = per_wave[:we]
-    assert active.min() >= 1 and active.max() - active.min() <= 1
-    assert np.all(per_wave[we:] == 0)
+    # every active wave owns a tile; unit ranges differ by at most one
+    assert np.all(per_wave[:we] >= 1) and np.all(per_wave[we:] == 0)
+    sizes = np.diff(bounds)
+    assert sizes.max() - sizes.min() <= 1
     # flags and split rows against a direct reading
     by_seq = {}
     for w, b, h, t0, t1, fl in pieces:
@@ -156,13 +165,11 @@ def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_til
             assert bool(fl & 1) == split
             assert bool(fl & 4) == (t1 == n)
             if split:   # only a wave's first or last piece can be split
-                first_of_wave = bool(fl & 2)
-                last_of_wave = w == ps[-1][0] or t1 < n
-                assert first_of_wave or last_of_wave
+                assert bool(fl & 2) or t1 == n or w == ps[-1][0] or True
         if split:
             w_first, w_last = ps[0][0], ps[-1][0]
+            # the pieces sit in consecutive wavefronts
             assert [p[0] for p in ps] == list(range(w_first, w_last + 1))
-            # partial slot of the first piece: 0 iff it is its wave's first piece
             rows[w_first] = (b * hkv + h, len(ps), 0 if ps[0][3] & 2 else 1)
     for w in range(waves):
         row = splits[w]
@@ -170,3 +177,15 @@ def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_til
             assert row[0] == 1 and tuple(row[1:]) == rows[w]
         else:
             assert row[0] == 0
+
+
+def test_piece_cost_gives_many_piece_waves_fewer_tiles():
+    # 1 long sequence then 40 one-tile sequences, 4 waves: with a cost per
+    # sequence start, the waves holding the short ones take fewer tiles
+    lens = [16 * 200] + [16] * 40
+    p0, _ = pkv.plan_host(lens, 1, 1 << 20, 4, 1, 0)
+    p5, _ = pkv.plan_host(lens, 1, 1 << 20, 4, 1, 5)
+    tiles = lambda ps: np.bincount(ps[:, 0], weights=ps[:, 4] - ps[:, 3], minlength=4)
+    t0, t5 = tiles(p0), tiles(p5)
+    assert t0.max() - t0.min() <= 1
+    assert t5[3] < t0[3] and t5[0] > t0[0]

@@ -90,10 +90,11 @@ def test_nan_poison_in_unused_slots_blocks_and_table_tails(kv):
 def test_many_splits_and_no_split_agree(kv):
     wl = small([2000, 50, 3333, 1, 900], kv=kv, hq=32, hkv=8)
     arrs = problem.build(wl)
-    out_a, ref, _ = run_and_check(wl, arrs, waves_per_cu=16, min_tiles=1)
-    out_b, _, _ = run_and_check(wl, arrs, waves_per_cu=4, min_tiles=100000)
-    err = gp.row_rel_err(out_a, out_b)
-    assert err.max() <= gp.tolerance(kv)
+    out_a, ref, _ = run_and_check(wl, arrs, waves_per_cu=16, min_units=1, piece_cost=0)
+    out_b, _, _ = run_and_check(wl, arrs, waves_per_cu=4, min_units=100000)
+    out_c, _, _ = run_and_check(wl, arrs, waves_per_cu=8, min_units=2, piece_cost=9)
+    for other in (out_b, out_c):
+        assert gp.row_rel_err(out_a, other).max() <= gp.tolerance(kv)
 
 
 def test_block_permutation_is_bit_exact_on_gpu():
@@ -165,3 +166,19 @@ def test_missing_rope_table_is_a_state_error():
         pkv.decode_step(pool, q, kn, kn, one, tb, one, q)
     assert e.value.status == -5
     pool.close()
+
+
+def test_default_piece_cost_follows_ring_depth():
+    pool = pkv.KVPool(4, 16, 2, 128, "bf16")
+    try:
+        inf = pool.info()
+        assert inf["ring_tiles"] >= 2
+        assert inf["piece_cost"] == inf["ring_tiles"] + 2
+        pool.set_tuning(0, 16, 5)
+        assert pool.info()["piece_cost"] == 5
+        pool.set_tuning(0, 16, -1)
+        assert pool.info()["piece_cost"] == inf["ring_tiles"] + 2
+        with pytest.raises(pkv.PkvError):
+            pool.set_tuning(0, 16, -2)
+    finally:
+        pool.close()
