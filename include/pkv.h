@@ -104,6 +104,8 @@ typedef struct pkv_pool_info {
   int32_t ring_tiles;        /* tiles each wavefront keeps in flight */
   int32_t min_units;         /* tuning in effect (kv_pool_set_tuning) */
   int32_t piece_cost;
+  int32_t young_weight_pct;
+  int32_t n_first;           /* wavefronts of the first workgroup on each CU */
 } pkv_pool_info;
 
 /* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
@@ -188,20 +190,30 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
  * context length outside [1, max_blocks_per_seq * block_size]. */
 pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 
-/* Tuning knobs (also read from PKV_WAVES_PER_CU, PKV_MIN_UNITS and
- * PKV_PIECE_COST at pool creation).  The step's work is measured in units:
- * one per 16-token tile, plus piece_cost for starting each (request, KV
- * head) sequence (its query rotation and append stall the wavefront's
- * loads), and split evenly over the wavefronts.  waves_per_cu: wavefronts
- * per compute unit (0 = as many as are resident at once, 8 on gfx950);
- * min_units: fewest units a wavefront is given before fewer wavefronts are
- * used (>= 1; raised to piece_cost + 1; default 16); piece_cost in [0, 64],
- * or -1 (the default) for ring_tiles + 2: a sequence start waits for the
- * wavefront's whole ring of in-flight tile loads (about ring_tiles
- * tile-times at full bandwidth) and then for its own query loads.
+/* Tuning knobs (also read from PKV_WAVES_PER_CU, PKV_MIN_UNITS,
+ * PKV_PIECE_COST and PKV_YOUNG_WEIGHT at pool creation).  The step's work is
+ * measured in units: one per 16-token tile, plus piece_cost for starting
+ * each (request, KV head) sequence (its query rotation and append stall the
+ * wavefront's loads), and split over the wavefronts in proportion to their
+ * weights (pkv_plan_host states the rule).
+ *  - waves_per_cu: wavefronts per compute unit (0 = as many as are resident
+ *    at once, 8 on gfx950).
+ *  - min_units: fewest units the lightest wavefront is given before fewer
+ *    wavefronts are used (>= 1; raised to piece_cost + 1; default 16).
+ *  - piece_cost: in [0, 64], or -1 (the default) for ring_tiles + 2.  A
+ *    sequence start waits for the wavefront's whole ring of in-flight tile
+ *    loads and then for its own query loads.
+ *  - young_weight_pct: share weight of the wavefronts of the later
+ *    workgroups on each compute unit, in percent of the first workgroup's
+ *    ([1, 100], or -1 for the default 65).  Two wavefronts on one SIMD
+ *    share its issue slots unevenly: the older streams 1.6-1.9x faster
+ *    while both run.  100 splits evenly.  The weights apply only to steps
+ *    with at least 256 units per launched wavefront (below that start-up
+ *    dominates and the split is even).
  * Synchronises the device. */
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
-                              int32_t min_units, int32_t piece_cost);
+                              int32_t min_units, int32_t piece_cost,
+                              int32_t young_weight_pct);
 
 /* Measurement.  While enabled, decode_step launches its two kernels (the
  * fused attention kernel and the split-merge kernel) with HIP start/stop
@@ -243,9 +255,18 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
  * lengths clamped to [0, max_tokens]) and costs its tiles plus piece_cost
  * units; its tile 0 owns the units [s, s + piece_cost], tile j >= 1 the unit
  * s + piece_cost + j.  The sequences' units are concatenated in (request,
- * head) order and split evenly over min(n_waves, ceil(C / max(min_units,
- * piece_cost + 1))) wavefronts; a wavefront takes the tiles whose first unit
- * falls in its range.  Writes up to max_pieces rows of 6 int32 to pieces:
+ * head) order, U in all.  If U >= weight_min_share * n_waves, wavefront w
+ * weighs weight_first if w < n_first, else weight_rest (1 <= weight_rest <=
+ * weight_first <= 1000); otherwise every wavefront weighs 1.  With Omega(w)
+ * the summed weight of wavefronts [0, w), W active wavefronts split the
+ * units at floor(U * Omega(w) / Omega(W)), and W is the largest value <=
+ * n_waves (and >= 1) whose lightest wavefront still gets at least m =
+ * max(min_units, piece_cost + 1) units: floor(U / m) if that is <= n_first,
+ * else the largest W with U * weight_rest >= m * Omega(W) (but at least
+ * n_first).  A wavefront takes the tiles whose first unit falls in its
+ * range.  decode_step uses n_first = the first workgroup on each compute
+ * unit (4 wavefronts per CU), weight_first = 100, weight_rest =
+ * young_weight_pct and weight_min_share = 256.  Writes up to max_pieces rows of 6 int32 to pieces:
  * {wave, request, kv_head, first_tile, end_tile, flags} with flags bit 0 =
  * the piece is part of a split sequence, bit 1 = it is the wave's first
  * piece, bit 2 = it is the last piece of its sequence; and n_waves rows of
@@ -254,8 +275,10 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
  * the first piece}, or zeros.  *n_pieces receives the total count. */
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
                          int32_t n_kv_heads, int32_t max_tokens, int32_t n_waves,
-                         int32_t min_units, int32_t piece_cost, int32_t max_pieces,
-                         int32_t* pieces, int32_t* n_pieces, int32_t* splits);
+                         int32_t min_units, int32_t piece_cost, int32_t n_first,
+                         int32_t weight_first, int32_t weight_rest,
+                         int32_t weight_min_share, int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
+                         int32_t* splits);
 
 /* Tokens per tile, the kernel's unit of work (16). */
 int32_t pkv_tile_tokens(void);

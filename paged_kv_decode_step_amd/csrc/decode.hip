@@ -352,7 +352,9 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   }
 
   const int64_t U = sP[B];                               // work units
-  const int64_t W = active_waves(U, p.n_waves, p.min_units);
+  const WaveWeights ww = weights_for(U, p.n_waves, p.weight_min_share,
+                                     WaveWeights{p.weight_first, p.weight_rest, p.n_first});
+  const int64_t W = active_waves(U, p.n_waves, p.min_units, ww);
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
   if (wave >= W) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
@@ -362,9 +364,9 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   Walk w0;
   int T;
   {
-    const TilePos t0 = tile_at_unit(sP, B, hkv, cost, wave_start(wave, U, W));
+    const TilePos t0 = tile_at_unit(sP, B, hkv, cost, wave_start(wave, U, W, ww));
     const int64_t g0 = global_tile(sP, t0.b, t0.h, t0.j, t0.n, hkv, cost);
-    const int64_t x1 = wave_start(wave + 1, U, W);
+    const int64_t x1 = wave_start(wave + 1, U, W, ww);
     int64_t g1 = (int64_t)sP[B] - (int64_t)hkv * cost * B;       // all tiles
     if (x1 < U) {
       const TilePos t1 = tile_at_unit(sP, B, hkv, cost, x1);
@@ -806,7 +808,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     }
     if (j0 == 0) {
       const int64_t last = first_unit(sP, cw.b, cw.h, cw.n - 1, cw.n, cost);
-      const int np = (int)(wave_of_unit(last, U, W) - wave + 1);
+      const int np = (int)(wave_of_unit(last, U, W, ww) - wave + 1);
       split_hdr = make_int4(1, cw.b * hkv + cw.h, np, slot);
     }
   };

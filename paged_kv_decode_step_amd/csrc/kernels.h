@@ -12,6 +12,7 @@ constexpr int kWaveThreads = 64;
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
 constexpr int kTileTokens = 16;    // tokens per KV tile (the unit of work)
 constexpr int kMaxPieceCost = 64;  // work units a sequence start may cost
+constexpr int kWeightMinShare = 256;  // units per wavefront for uneven weights
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -42,6 +43,10 @@ struct DecodeParams {
   int32_t n_waves;           // wavefronts launched (multiple of 4)
   int32_t min_units;         // fewest work units a wavefront is given (> piece_cost)
   int32_t piece_cost;        // work units a sequence costs on top of its tiles
+  int32_t n_first;           // wavefronts of the first workgroup on each compute unit
+  int32_t weight_first;      // their share weight ...
+  int32_t weight_rest;       // ... and that of the others (weight_first >= weight_rest >= 1)
+  int32_t weight_min_share;  // units per wavefront below which the weights are even
   float sm_scale_log2;       // log2(e) / sqrt(D)
 };
 

@@ -61,6 +61,15 @@ int resolve_piece_cost(int requested, int ring_tiles) {
   return std::max(0, std::min(c, pkv::kMaxPieceCost));
 }
 
+// Share weight of the wavefronts of later workgroups on a compute unit, in
+// percent of the first workgroup's.  Two wavefronts on one SIMD do not
+// stream alike: the older wins most issue slots and, while both run, moves
+// 1.6-1.9x the younger's bytes; -1 asks for 65%.
+int resolve_young_pct(int requested) {
+  const int v = requested < 0 ? 65 : requested;
+  return std::max(1, std::min(v, 100));
+}
+
 }  // namespace
 
 struct pkv_pool {
@@ -89,6 +98,7 @@ struct pkv_pool {
   int min_units = 16;
   int piece_cost = 0;       // resolved (never the automatic -1)
   int ring_tiles = 0;
+  int young_pct = 100;      // share weight of later workgroups, % of the first's
   // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -209,6 +219,7 @@ pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_h
   p->min_units = std::max(1, env_int("PKV_MIN_UNITS", 16));
   p->ring_tiles = pkv::decode_ring_tiles(kv_kind(kv_dtype), head_dim);
   p->piece_cost = resolve_piece_cost(env_int("PKV_PIECE_COST", -1), p->ring_tiles);
+  p->young_pct = resolve_young_pct(env_int("PKV_YOUNG_WEIGHT", -1));
   pkv_status s = size_workspace(p, env_int("PKV_WAVES_PER_CU", 0));
   if (s != PKV_OK) { free_pool(p); return s; }
   *out_pool = p;
@@ -298,16 +309,20 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->ring_tiles = pool->ring_tiles;
   info->min_units = pool->min_units;
   info->piece_cost = pool->piece_cost;
+  info->young_weight_pct = pool->young_pct;
+  info->n_first = std::min(pool->n_waves, 4 * pool->cus);
   return PKV_OK;
 }
 
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_units,
-                              int32_t piece_cost) {
+                              int32_t piece_cost, int32_t young_weight_pct) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
   if (min_units < 1) return fail(PKV_ERR_INVALID, "min_units must be >= 1");
   if (piece_cost < -1 || piece_cost > pkv::kMaxPieceCost)
     return fail(PKV_ERR_INVALID, "piece_cost must be -1 (automatic) or in [0, %d]",
                 pkv::kMaxPieceCost);
+  if (young_weight_pct < -1 || young_weight_pct == 0 || young_weight_pct > 100)
+    return fail(PKV_ERR_INVALID, "young_weight_pct must be -1 (automatic) or in [1, 100]");
   if (waves_per_cu < 0 || waves_per_cu > 32)
     return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
   int cur = 0;
@@ -319,6 +334,7 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
   if (s != PKV_OK) return s;
   pool->min_units = min_units;
   pool->piece_cost = resolve_piece_cost(piece_cost, pool->ring_tiles);
+  pool->young_pct = resolve_young_pct(young_weight_pct);
   return PKV_OK;
 }
 
@@ -460,6 +476,11 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.n_waves = pool->n_waves;
   p.piece_cost = pool->piece_cost;
   p.min_units = std::max(pool->min_units, pool->piece_cost + 1);
+  // the first workgroup dispatched to each compute unit: 4 wavefronts per CU
+  p.n_first = std::min(pool->n_waves, 4 * pool->cus);
+  p.weight_first = 100;
+  p.weight_rest = pool->young_pct;
+  p.weight_min_share = pkv::kWeightMinShare;
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
@@ -521,7 +542,9 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
 
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
                          int32_t max_tokens, int32_t n_waves, int32_t min_units,
-                         int32_t piece_cost, int32_t max_pieces, int32_t* pieces,
+                         int32_t piece_cost, int32_t n_first, int32_t weight_first,
+                         int32_t weight_rest, int32_t weight_min_share,
+                         int32_t max_pieces, int32_t* pieces,
                          int32_t* n_pieces, int32_t* splits) {
   if (!context_lens || !n_pieces || !splits || (max_pieces > 0 && !pieces))
     return fail(PKV_ERR_INVALID, "null argument");
@@ -529,12 +552,17 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
     return fail(PKV_ERR_INVALID, "sizes must be positive");
   if (piece_cost < 0 || piece_cost > pkv::kMaxPieceCost)
     return fail(PKV_ERR_INVALID, "piece_cost must be in [0, %d]", pkv::kMaxPieceCost);
+  if (n_first < 0 || weight_rest < 1 || weight_first < weight_rest || weight_first > 1000)
+    return fail(PKV_ERR_INVALID, "need n_first >= 0 and 1 <= weight_rest <= weight_first <= 1000");
+  if (weight_min_share < 0) return fail(PKV_ERR_INVALID, "weight_min_share must be >= 0");
   const int hkv = n_kv_heads, cost = piece_cost;
   std::vector<int> P(batch + 1, 0);
   for (int b = 0; b < batch; ++b)
     P[b + 1] = P[b] + hkv * (pkv::tiles_of(context_lens[b], max_tokens) + cost);
   const int64_t C = P[batch];
-  const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1));
+  const pkv::WaveWeights ww = pkv::weights_for(
+      C, n_waves, weight_min_share, pkv::WaveWeights{weight_first, weight_rest, n_first});
+  const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1), ww);
   const int64_t n_tiles = (int64_t)P[batch] - (int64_t)hkv * cost * batch;
   for (int64_t w = 0; w < n_waves; ++w) {
     int32_t* row = splits + 4 * w;
@@ -542,10 +570,10 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
   }
   int64_t count = 0;
   for (int64_t w = 0; w < W; ++w) {
-    pkv::TilePos t = pkv::tile_at_unit(P.data(), batch, hkv, cost, pkv::wave_start(w, C, W));
+    pkv::TilePos t = pkv::tile_at_unit(P.data(), batch, hkv, cost, pkv::wave_start(w, C, W, ww));
     const int64_t g0 = pkv::global_tile(P.data(), t.b, t.h, t.j, t.n, hkv, cost);
     int64_t g1 = n_tiles;
-    const int64_t x1 = pkv::wave_start(w + 1, C, W);
+    const int64_t x1 = pkv::wave_start(w + 1, C, W, ww);
     if (x1 < C) {
       const pkv::TilePos t1 = pkv::tile_at_unit(P.data(), batch, hkv, cost, x1);
       g1 = pkv::global_tile(P.data(), t1.b, t1.h, t1.j, t1.n, hkv, cost);
@@ -581,7 +609,7 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
         const int64_t last = pkv::first_unit(P.data(), t.b, t.h, t.n - 1, t.n, cost);
         row[0] = 1;
         row[1] = t.b * hkv + t.h;
-        row[2] = (int32_t)(pkv::wave_of_unit(last, C, W) - w + 1);
+        row[2] = (int32_t)(pkv::wave_of_unit(last, C, W, ww) - w + 1);
         row[3] = first ? 0 : 1;
       }
       first = false;

@@ -14,17 +14,28 @@
 //    starting it (the query rotation and, at its end, the append; a
 //    wavefront pays these with its loads stalled), and its first tile owns
 //    the A + 1 units [s, s + A], tile j >= 1 the unit s + A + j;
-//  * sequences are concatenated in (b, h) order: C units in all;
-//  * wavefront w of W active ones takes the units [w*C/W, (w+1)*C/W), i.e.
-//    the tiles whose first unit falls there, so wavefronts that start many
-//    short sequences get fewer tiles and all of them finish together;
+//  * sequences are concatenated in (b, h) order: U units in all;
+//  * wavefront w has a weight: the first n_first wavefronts (the first
+//    workgroup that lands on each compute unit) weigh wa, the others wb.
+//    Two wavefronts that share a SIMD do not progress alike: the older one
+//    wins most issue slots and streams 1.6-1.9x faster while both run, so
+//    equal shares leave the younger ones finishing long after.  The
+//    weights apply only with at least min_share units per wavefront;
+//    below that, start-up dominates and the weights are even;  With
+//    Omega(w) the summed weight of wavefronts [0, w), wavefront w of W
+//    active ones takes the units [U Omega(w) / Omega(W), U Omega(w+1) /
+//    Omega(W)), i.e. the tiles whose first unit falls there;
+//  * W is the most wavefronts (at most n_waves) that still give the
+//    lightest one min_units units, and min_units > A: every window of A + 1
+//    consecutive units holds the first unit of some tile, so every active
+//    wavefront owns at least one tile;
 //  * a sequence cut between wavefronts ("split") leaves one partial softmax
 //    state per piece; a second kernel merges them.
 //
 // A split sequence starts in exactly one wavefront (as that wavefront's last
-// piece) and its pieces sit in consecutive wavefronts (every wavefront owns
-// at least one tile when W <= C / (A + 1)).  A wavefront keeps at most two
-// partial states: slot 0 for its first piece, slot 1 for its last piece.
+// piece) and its pieces sit in consecutive wavefronts.  A wavefront keeps at
+// most two partial states: slot 0 for its first piece, slot 1 for its last
+// piece.
 #pragma once
 
 #include <stdint.h>
@@ -53,22 +64,54 @@ PKV_HD inline int tiles_of(int L, int cap) {
   return n < 1 ? 1 : n;
 }
 
-// Active wavefronts: all of them, unless that leaves fewer than min_units
-// work units each.  Never more than C, so every active wavefront has work.
-PKV_HD inline int64_t active_waves(int64_t n_units, int64_t n_waves, int64_t min_units) {
-  int64_t by_min = (n_units + min_units - 1) / min_units;
-  if (by_min < 1) by_min = 1;
-  return n_waves < by_min ? n_waves : by_min;
+// Weights of the wavefronts: [0, n_first) weigh wa, the rest wb (wa >= wb >= 1).
+struct WaveWeights {
+  int64_t wa, wb, n_first;
+};
+
+// The weights in force for a step of n_units units: the given ones when
+// there are at least min_share units per launched wavefront, else even
+// weights (with a few tiles per wavefront the start-up dominates and the
+// older wavefront has no time to pull ahead).
+PKV_HD inline WaveWeights weights_for(int64_t n_units, int64_t n_waves, int64_t min_share,
+                                      const WaveWeights& k) {
+  if (n_units >= min_share * n_waves) return k;
+  return WaveWeights{1, 1, k.n_first};
 }
 
-PKV_HD inline int64_t wave_start(int64_t w, int64_t n_units, int64_t n_active) {
-  return (w * n_units) / n_active;
+// Omega(w): summed weight of wavefronts [0, w).
+PKV_HD inline int64_t cum_weight(int64_t w, const WaveWeights& k) {
+  return w <= k.n_first ? k.wa * w : k.wa * k.n_first + k.wb * (w - k.n_first);
 }
 
-// The wavefront whose unit range holds unit u: the largest w with
-// wave_start(w) <= u.
-PKV_HD inline int64_t wave_of_unit(int64_t u, int64_t n_units, int64_t n_active) {
-  return ((u + 1) * n_active - 1) / n_units;
+// Largest w >= 0 with Omega(w) <= x, for x >= 0.
+PKV_HD inline int64_t weight_index(int64_t x, const WaveWeights& k) {
+  const int64_t f = k.wa * k.n_first;
+  return x < f ? x / k.wa : k.n_first + (x - f) / k.wb;
+}
+
+// Active wavefronts: the most (at most n_waves, at least 1) whose lightest
+// member still gets min_units units, U * weight / Omega(W) >= min_units.
+PKV_HD inline int64_t active_waves(int64_t n_units, int64_t n_waves, int64_t min_units,
+                                   const WaveWeights& k) {
+  int64_t W = n_units / min_units;                 // all of weight wa
+  if (W > k.n_first) W = weight_index(n_units * k.wb / min_units, k);
+  if (W < k.n_first && n_units / min_units >= k.n_first) W = k.n_first;
+  if (W > n_waves) W = n_waves;
+  return W < 1 ? 1 : W;
+}
+
+PKV_HD inline int64_t wave_start(int64_t w, int64_t n_units, int64_t n_active,
+                                 const WaveWeights& k) {
+  return n_units * cum_weight(w, k) / cum_weight(n_active, k);
+}
+
+// The wavefront whose unit range holds unit u: the largest w < n_active
+// with wave_start(w) <= u.
+PKV_HD inline int64_t wave_of_unit(int64_t u, int64_t n_units, int64_t n_active,
+                                   const WaveWeights& k) {
+  const int64_t w = weight_index(((u + 1) * cum_weight(n_active, k) - 1) / n_units, k);
+  return w < n_active - 1 ? w : n_active - 1;
 }
 
 // Largest b in [0, B) with P[b] <= pos, for a non-decreasing prefix array

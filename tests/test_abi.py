@@ -100,11 +100,15 @@ def test_tile_tokens():
 
 
 # ---- work partition ---------------------------------------------------------
-def reference_partition(lens, hkv, cap, n_waves, min_units, cost):
+def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=1, wr=1,
+                        min_share=0):
     """The partition written out plainly: sequences (b, h) in order, each cut
     into max(1, ceil(min(L, cap)/16)) tiles and costing its tiles plus
-    `cost` units (tile 0 owns cost + 1 units), the units split evenly and
-    each tile owned by the wave holding its first unit."""
+    `cost` units (tile 0 owns cost + 1 units); wave w weighs wf if
+    w < n_first else wr; the most waves whose every member's exact share
+    is >= max(min_units, cost + 1) units are used (found by trying every
+    count); the units are cut at floor(total * weights before w / all
+    weights) and each tile is owned by the wave holding its first unit."""
     ns = [max(1, -(-min(max(int(L), 0), cap) // 16)) for L in lens]
     seqs = [(b, h, ns[b]) for b in range(len(lens)) for h in range(hkv)]
     first_units = []
@@ -114,32 +118,60 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost):
             first_units.append(((b, h, t), u))
             u += cost + 1 if t == 0 else 1
     total = u
-    we = min(n_waves, max(1, -(-total // max(min_units, cost + 1))))
-    bounds = [(w * total) // we for w in range(we + 1)]
+    m = max(min_units, cost + 1)
+    if total < min_share * n_waves:     # too little work per wave: even weights
+        wf = wr = 1
+    weight = [wf if w < n_first else wr for w in range(n_waves)]
+
+    def enough(count):
+        om = sum(weight[:count])
+        return all(total * weight[w] >= m * om for w in range(count))
+
+    we = max([c for c in range(1, n_waves + 1) if enough(c)], default=1)
+    om = sum(weight[:we])
+    bounds = [(total * sum(weight[:w])) // om for w in range(we + 1)]
     owner = {}
     for key, fu in first_units:
         owner[key] = max(i for i in range(we) if bounds[i] <= fu)
     return owner, bounds, we, seqs
 
 
-@pytest.mark.parametrize("lens,hkv,waves,min_units,cost", [
-    ([138, 1012, 84], 4, 64, 4, 0),
-    ([138, 1012, 84], 4, 64, 4, 3),
-    ([1, 1, 1, 1], 2, 64, 1, 0),
-    ([1, 1, 1, 1], 2, 64, 1, 2),
-    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 0),
-    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 5),
-    ([1], 1, 8, 4, 3),
-    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3, 3),
-    (list(np.random.default_rng(1).integers(1, 200, 60)), 4, 200, 1, 7),
-    ([100] * 7, 2, 1000, 1, 1),       # more wavefronts than units allow
-    ([0, -5, 40], 2, 16, 1, 2),       # invalid lengths still get one tile
-    ([16, 17, 15, 32, 33], 1, 5, 1, 0),
+@pytest.mark.parametrize("lens,hkv,waves,min_units,cost,nf,wf,wr", [
+    ([138, 1012, 84], 4, 64, 4, 0, 0, 1, 1),
+    ([138, 1012, 84], 4, 64, 4, 3, 0, 1, 1),
+    ([138, 1012, 84], 4, 64, 4, 3, 32, 100, 57),
+    ([1, 1, 1, 1], 2, 64, 1, 0, 0, 1, 1),
+    ([1, 1, 1, 1], 2, 64, 1, 2, 0, 1, 1),
+    ([1, 1, 1, 1], 2, 64, 1, 2, 4, 3, 2),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 0, 0, 1, 1),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 5, 0, 1, 1),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 2, 5, 10, 7, 4),
+    ([5000, 3, 70, 31, 32, 33], 3, 20, 9, 5, 4, 1000, 1),
+    ([1], 1, 8, 4, 3, 0, 1, 1),
+    ([1], 1, 8, 4, 3, 4, 100, 57),
+    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3, 3, 0, 1, 1),
+    (list(np.random.default_rng(0).integers(1, 3000, 40)), 8, 96, 3, 3, 48, 100, 57),
+    (list(np.random.default_rng(1).integers(1, 200, 60)), 4, 200, 1, 7, 0, 1, 1),
+    (list(np.random.default_rng(1).integers(1, 200, 60)), 4, 200, 1, 7, 100, 100, 40),
+    (list(np.random.default_rng(2).integers(1, 5000, 30)), 8, 64, 16, 8, 32, 100, 57),
+    ([100] * 7, 2, 1000, 1, 1, 0, 1, 1),       # more wavefronts than units allow
+    ([100] * 7, 2, 1000, 1, 1, 500, 100, 57),
+    ([0, -5, 40], 2, 16, 1, 2, 0, 1, 1),       # invalid lengths still get one tile
+    ([16, 17, 15, 32, 33], 1, 5, 1, 0, 0, 1, 1),
+    ([16, 17, 15, 32, 33], 1, 5, 1, 0, 2, 5, 3),
+    ([9 * 16 - 3], 1, 2, 16, 8, 0, 1, 1),     # U = m + 1
+    ([23, 10], 2, 64, 6, 5, 0, 1, 1),         # ceil(U/m) = 5 waves would leave wave 3 no tile
 ])
-def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_units, cost):
+@pytest.mark.parametrize("min_share", [0, 40])
+def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_units, cost,
+                                                       nf, wf, wr, min_share):
     cap = 1 << 20
-    pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_units, cost)
-    owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_units, cost)
+    pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_units, cost, nf, wf, wr,
+                                   min_share)
+    owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_units, cost,
+                                                  nf, wf, wr, min_share)
+    if bounds[-1] < min_share * waves:
+        wf = wr = 1
     seen = {}
     per_wave = np.zeros(waves, dtype=np.int64)
     for w, b, h, t0, t1, fl in pieces:
@@ -149,10 +181,12 @@ def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_uni
             seen[(b, h, t)] = w
         per_wave[w] += t1 - t0
     assert seen == owner
-    # every active wave owns a tile; unit ranges differ by at most one
+    # every active wave owns a tile; unit ranges within one of their exact shares
     assert np.all(per_wave[:we] >= 1) and np.all(per_wave[we:] == 0)
     sizes = np.diff(bounds)
-    assert sizes.max() - sizes.min() <= 1
+    weights = np.array([wf if w < nf else wr for w in range(we)], dtype=np.float64)
+    exact = bounds[-1] * weights / weights.sum()
+    assert np.all(np.abs(sizes - exact) < 1.0)
     # flags and split rows against a direct reading
     by_seq = {}
     for w, b, h, t0, t1, fl in pieces:

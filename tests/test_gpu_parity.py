@@ -93,7 +93,12 @@ def test_many_splits_and_no_split_agree(kv):
     out_a, ref, _ = run_and_check(wl, arrs, waves_per_cu=16, min_units=1, piece_cost=0)
     out_b, _, _ = run_and_check(wl, arrs, waves_per_cu=4, min_units=100000)
     out_c, _, _ = run_and_check(wl, arrs, waves_per_cu=8, min_units=2, piece_cost=9)
-    for other in (out_b, out_c):
+    # later workgroups weighted down to almost nothing, and evenly weighted
+    out_d, _, _ = run_and_check(wl, arrs, waves_per_cu=8, min_units=1, piece_cost=0,
+                                young_weight=1)
+    out_e, _, _ = run_and_check(wl, arrs, waves_per_cu=12, min_units=1, piece_cost=2,
+                                young_weight=100)
+    for other in (out_b, out_c, out_d, out_e):
         assert gp.row_rel_err(out_a, other).max() <= gp.tolerance(kv)
 
 
