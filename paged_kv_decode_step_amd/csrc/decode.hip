@@ -65,7 +65,12 @@
 #define PKV_RING_BYTES 32768
 #endif
 #ifndef PKV_RING_BYTES_FP8
-#define PKV_RING_BYTES_FP8 24576
+#define PKV_RING_BYTES_FP8 16384
+#endif
+// Bytes of LDS per wavefront that hold the global writes of the tile loop
+// (output rows, appended rows, the first partial state) until the loop ends.
+#ifndef PKV_QUEUE_BYTES
+#define PKV_QUEUE_BYTES 10240
 #endif
 // Resident wavefronts per SIMD the attention kernel is compiled for (its
 // register budget is 512 / this).
@@ -113,6 +118,13 @@ __device__ __forceinline__ float sum_over_lq(float v) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wait for every vector memory operation of the wavefront (vmcnt 0; the
+// other counters untouched).  Ends a rarely taken branch that stores inside
+// the tile loop: the stores are then complete where the branch rejoins, and
+// the waits for tile loads that follow keep their exact in-order counts
+// instead of degrading to full drains on every path.
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // float32 -> bfloat16 bits, round to nearest even (finite), quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -311,6 +323,16 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   __shared__ int sWsum[kBlockThreads / 64];
   __shared__ u32x4_t sKrow[kBlockThreads / 64][C::KROWS];   // appended key row
   __shared__ uint32_t sVrow[kBlockThreads / 64][D];          // appended value codes
+  // Per-wavefront queue of deferred global writes.  On gfx950 stores and
+  // loads share one completion counter and may complete out of order with
+  // respect to each other, so the first wait for a tile load after any store
+  // has to drain every load in flight.  Writes made inside the tile loop are
+  // therefore parked here and issued once the wavefront's tiles are done; a
+  // write that does not fit is made at once.  Items: a 16-byte header
+  // {type | words << 4, request * Hkv + head, block, slot of the new token}
+  // and `words` 16-byte payload words.
+  constexpr int QW = PKV_QUEUE_BYTES / 16;
+  __shared__ u32x4_t sQ[kBlockThreads / 64][QW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -454,6 +476,50 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 
   const int64_t out_row_stride = (int64_t)hkv * G;   // query heads per request
 
+  enum : uint32_t { Q_OUT = 0, Q_APPEND = 1, Q_PART = 2 };
+  constexpr int IO_BYTES = C::IO_BF16 ? 2 : 4;
+  const int out_words = G * D * IO_BYTES / 16;            // G output rows
+  constexpr int app_words = C::KROWS + D / 4;             // key row + value codes (u32)
+  const int part_words = G * 4 * C::NT + (G + 1) / 2;     // G*4 lanes' accumulators + (m, l)
+  int q_used = 0;      // words of sQ[wid] in use
+  uint32_t* const sQw = reinterpret_cast<uint32_t*>(&sQ[wid][0]);
+
+  // Room for an item of `words` payload words: the word index of its
+  // header, or -1 (the write is then made at once).
+  auto q_reserve = [&](int words) __attribute__((always_inline)) -> int {
+    if (q_used + 1 + words > QW) return -1;
+    const int at = q_used;
+    q_used += 1 + words;
+    return at;
+  };
+  auto q_header = [&](int at, uint32_t type, int words, int seq, int blk, int r) __attribute__((always_inline)) {
+    if (lane == 0) {
+      u32x4_t hd;
+      hd[0] = type | ((uint32_t)words << 4);
+      hd[1] = (uint32_t)seq;
+      hd[2] = (uint32_t)blk;
+      hd[3] = (uint32_t)r;
+      sQ[wid][at] = hd;
+    }
+  };
+  // Global writes of the appended rows (codes as u32 per value dim).
+  auto write_append = [&](int h, int blk, int r, const u32x4_t* krow, const uint32_t* vcodes)
+      __attribute__((always_inline)) {
+    const int64_t toff = (((int64_t)blk * hkv + h) * C::TPB + ((r / kTileTokens) & (C::TPB - 1))) *
+                         C::TILE_BYTES;
+    const int r16 = r & 15;
+    if (lane < C::KROWS) *reinterpret_cast<u32x4_t*>(kpool + toff + (lane * 16 + r16) * 16) = krow[lane];
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int d = lane + 64 * k;
+      const uint32_t code = vcodes[d];
+      char* dst = vpool + toff + v_elem_offset<KV, D, BS>(r16, d);
+      if constexpr (C::ELEM == 4) *reinterpret_cast<uint32_t*>(dst) = code;
+      else if constexpr (C::ELEM == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)code;
+      else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)code;
+    }
+  };
+
   auto begin_piece = [&](int i) __attribute__((always_inline)) {
     const int b = cw.b, h = cw.h;
     const int Lraw = lens[b];
@@ -595,8 +661,6 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
         bad_block |= 1u;
         blk = 0;
       }
-      const int64_t toff = (((int64_t)blk * hkv + h) * C::TPB + (((L - 1) / kTileTokens) & (C::TPB - 1))) *
-                           C::TILE_BYTES;
       const int64_t nrow = ((int64_t)b * hkv + h) * D;
       float inv_k = 1.0f, inv_v = 1.0f;
       if constexpr (KV == KV_FP8) {
@@ -629,18 +693,25 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
           for (int k = 0; k < 4 / C::ELEM; ++k) w |= enc[i2 * (4 / C::ELEM) + k] << (k * C::ELEM * 8);
           row[i2] = w;
         }
-        *reinterpret_cast<u32x4_t*>(kpool + toff + (lane * 16 + r0) * 16) = row;
         sKrow[wid][lane] = row;
       }
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
         const int d = lane + 64 * k;
         const uint32_t code = encode_kv<KV>(load_io<C::IO_BF16>(p.v_new, nrow + d), inv_v);
-        char* dst = vpool + toff + v_elem_offset<KV, D, BS>(r0, d);
-        if constexpr (C::ELEM == 4) *reinterpret_cast<uint32_t*>(dst) = code;
-        else if constexpr (C::ELEM == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)code;
-        else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)code;
         sVrow[wid][d] = code;
+      }
+      // the global write of the rows: queued (a copy), or made now
+      const int at = q_reserve(app_words);
+      const int r = (L - 1) & (BS - 1);
+      if (at >= 0) {
+        q_header(at, Q_APPEND, app_words, b * hkv + h, blk, r);
+        if (lane < C::KROWS) sQ[wid][at + 1 + lane] = sKrow[wid][lane];
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) sQw[(at + 1 + C::KROWS) * 4 + lane + 64 * k] = sVrow[wid][lane + 64 * k];
+      } else {
+        write_append(h, blk, r, &sKrow[wid][0], &sVrow[wid][0]);
+        wait_vector_memory();
       }
     }
     m_run = -INFINITY;
@@ -773,21 +844,29 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     }
   };
 
+  // The G output rows of sequence (b, h), normalised and cast: queued as
+  // an item laid out like the rows in memory ([head][dim]), or stored now.
   auto store_out = [&](int b, int h, const f32x4_t (&o)[C::NT], float scale) __attribute__((always_inline)) {
+    const int at = q_reserve(out_words);
+    if (at >= 0) q_header(at, Q_OUT, out_words, b * hkv + h, 0, 0);
     if (lr >= G) return;
     const int64_t row = ((int64_t)b * out_row_stride + h * G + lr) * D;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const int d = 16 * nt + 4 * lq;
+      const int e = (at + 1) * (16 / IO_BYTES) + lr * D + d;     // io element index in sQ[wid]
       if constexpr (C::IO_BF16) {
         u32x2_t w;
         w[0] = bf16_rne(o[nt][0] * scale) | (bf16_rne(o[nt][1] * scale) << 16);
         w[1] = bf16_rne(o[nt][2] * scale) | (bf16_rne(o[nt][3] * scale) << 16);
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = w;
+        if (at >= 0) *reinterpret_cast<u32x2_t*>(sQw + e / 2) = w;
+        else *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = w;
       } else {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = o[nt] * scale;
+        if (at >= 0) *reinterpret_cast<f32x4_t*>(sQw + e) = o[nt] * scale;
+        else *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = o[nt] * scale;
       }
     }
+    if (at < 0) wait_vector_memory();
   };
 
   auto end_piece = [&]() __attribute__((always_inline)) {
@@ -796,15 +875,33 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       store_out(cw.b, cw.h, acc, lt > 0.f ? vsc / lt : 0.f);
       return;
     }
-    float* part = p.partials + ((int64_t)wave * 2 + slot) * PF;
-    if (lr < G) {
+    // The wavefront's first piece is queued (more tiles follow); its last
+    // piece ends its tiles and is stored now.
+    const int at = slot == 0 ? q_reserve(part_words) : -1;
+    if (at >= 0) {
+      q_header(at, Q_PART, part_words, cw.b * hkv + cw.h, 0, 0);
+      if (lr < G) {
+        f32x4_t* accq = reinterpret_cast<f32x4_t*>(&sQ[wid][at + 1]);
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-        *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = acc[nt] * vsc;
-      if (lq == 0) {
-        part[16 * D + 2 * lr] = m_run;
-        part[16 * D + 2 * lr + 1] = lt;
+        for (int nt = 0; nt < C::NT; ++nt) accq[(lq * G + lr) * C::NT + nt] = acc[nt] * vsc;
+        if (lq == 0) {
+          float* ml = reinterpret_cast<float*>(&sQ[wid][at + 1 + G * 4 * C::NT]);
+          ml[2 * lr] = m_run;
+          ml[2 * lr + 1] = lt;
+        }
       }
+    } else {
+      float* part = p.partials + ((int64_t)wave * 2 + slot) * PF;
+      if (lr < G) {
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+          *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = acc[nt] * vsc;
+        if (lq == 0) {
+          part[16 * D + 2 * lr] = m_run;
+          part[16 * D + 2 * lr + 1] = lt;
+        }
+      }
+      wait_vector_memory();
     }
     if (j0 == 0) {
       const int64_t last = first_unit(sP, cw.b, cw.h, cw.n - 1, cw.n, cost);
@@ -834,6 +931,37 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
         walk_next(cw, sP, B, hkv, cost);
       }
     }, std::make_integer_sequence<int, R>{});
+  }
+
+  // ---- the queued writes, in order
+  for (int off = 0; off < q_used;) {
+    const u32x4_t hd = sQ[wid][off];
+    const uint32_t type = (uint32_t)uniform((int)(hd[0] & 15u));
+    const int words = uniform((int)(hd[0] >> 4));
+    const int seq = uniform((int)hd[1]);
+    const int b = seq / hkv, h = seq - b * hkv;
+    const u32x4_t* pl = &sQ[wid][off + 1];
+    if (type == Q_OUT) {
+      char* dst = static_cast<char*>(p.out) + ((int64_t)b * out_row_stride + h * G) * D * IO_BYTES;
+      for (int w = lane; w < words; w += 64) *reinterpret_cast<u32x4_t*>(dst + (int64_t)w * 16) = pl[w];
+    } else if (type == Q_APPEND) {
+      write_append(h, uniform((int)hd[2]), uniform((int)hd[3]), pl,
+                   reinterpret_cast<const uint32_t*>(pl + C::KROWS));
+    } else {                                   // partial state of the first piece (slot 0)
+      float* part = p.partials + (int64_t)wave * 2 * PF;
+      if (lr < G) {
+        const f32x4_t* accq = reinterpret_cast<const f32x4_t*>(pl);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+          *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = accq[(lq * G + lr) * C::NT + nt];
+        if (lq == 0) {
+          const float* ml = reinterpret_cast<const float*>(pl + G * 4 * C::NT);
+          part[16 * D + 2 * lr] = ml[2 * lr];
+          part[16 * D + 2 * lr + 1] = ml[2 * lr + 1];
+        }
+      }
+    }
+    off += 1 + words;
   }
 
   if (bad_block | bad_len | bad_pos) {
