@@ -480,7 +480,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   constexpr int IO_BYTES = C::IO_BF16 ? 2 : 4;
   const int out_words = G * D * IO_BYTES / 16;            // G output rows
   constexpr int app_words = C::KROWS + D / 4;             // key row + value codes (u32)
-  const int part_words = G * 4 * C::NT + (G + 1) / 2;     // G*4 lanes' accumulators + (m, l)
+  const int part_words = G * D / 4 + (G + 1) / 2;         // [head][dim] accumulators + (m, l)
   int q_used = 0;      // words of sQ[wid] in use
   uint32_t* const sQw = reinterpret_cast<uint32_t*>(&sQ[wid][0]);
 
@@ -883,9 +883,9 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       if (lr < G) {
         f32x4_t* accq = reinterpret_cast<f32x4_t*>(&sQ[wid][at + 1]);
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) accq[(lq * G + lr) * C::NT + nt] = acc[nt] * vsc;
+        for (int nt = 0; nt < C::NT; ++nt) accq[(lr * D + 16 * nt + 4 * lq) / 4] = acc[nt] * vsc;
         if (lq == 0) {
-          float* ml = reinterpret_cast<float*>(&sQ[wid][at + 1 + G * 4 * C::NT]);
+          float* ml = reinterpret_cast<float*>(&sQ[wid][at + 1 + G * D / 4]);
           ml[2 * lr] = m_run;
           ml[2 * lr + 1] = lt;
         }
@@ -895,7 +895,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       if (lr < G) {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
-          *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = acc[nt] * vsc;
+          *reinterpret_cast<f32x4_t*>(part + lr * D + 16 * nt + 4 * lq) = acc[nt] * vsc;
         if (lq == 0) {
           part[16 * D + 2 * lr] = m_run;
           part[16 * D + 2 * lr + 1] = lt;
@@ -949,16 +949,11 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
                    reinterpret_cast<const uint32_t*>(pl + C::KROWS));
     } else {                                   // partial state of the first piece (slot 0)
       float* part = p.partials + (int64_t)wave * 2 * PF;
-      if (lr < G) {
-        const f32x4_t* accq = reinterpret_cast<const f32x4_t*>(pl);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-          *reinterpret_cast<f32x4_t*>(part + lane * (4 * C::NT) + 4 * nt) = accq[(lq * G + lr) * C::NT + nt];
-        if (lq == 0) {
-          const float* ml = reinterpret_cast<const float*>(pl + G * 4 * C::NT);
-          part[16 * D + 2 * lr] = ml[2 * lr];
-          part[16 * D + 2 * lr + 1] = ml[2 * lr + 1];
-        }
+      for (int w = lane; w < G * D / 4; w += 64) *reinterpret_cast<u32x4_t*>(part + 4 * w) = pl[w];
+      if (lane < G) {
+        const float* ml = reinterpret_cast<const float*>(pl + G * D / 4);
+        part[16 * D + 2 * lane] = ml[2 * lane];
+        part[16 * D + 2 * lane + 1] = ml[2 * lane + 1];
       }
     }
     off += 1 + words;
@@ -978,73 +973,98 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 // Merge the partial softmax states of each split sequence (one wavefront per
 // sequence, found from the header its first wavefront left):
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
-// Pieces are read four at a time, with the running maximum rescaling the
-// sums, so the loads of a batch are all in flight together.
-template <bool IO_BF16, int D>
+// A piece's accumulators are G*D floats in [head][dim] order; lane l takes
+// the 16-byte chunks l + 64k (k < KC) of every piece, so all 64 lanes work
+// and a batch of 32/KC pieces is in flight at once, with the running maximum
+// rescaling the sums between batches.
+template <bool IO_BF16, int D, int KC>
 __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParams p) {
-  constexpr int NT = D / 16;
   constexpr int PF = partial_floats(D);
-  constexpr int KB = 4;
+  constexpr int PPB = 32 / KC;                  // pieces per batch
   const int lane = threadIdx.x & 63;
   const int w = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
   const int4 hdr = p.headers[w];
   if (!uniform(hdr.x)) return;
-  const int lr = lane & 15, lq = lane >> 4;
   const int G = p.group, hkv = p.n_kv_heads;
-  if (lr >= G) return;
   const int seq = uniform(hdr.y), np = uniform(hdr.z), slot0 = uniform(hdr.w);
   const int b = seq / hkv, h = seq - (seq / hkv) * hkv;
-  float M = -INFINITY, den = 0.f;
-  f32x4_t num[NT];
+  const int nchunk = G * D / 4;
+  int ch[KC], hd[KC];
+  bool ok[KC];
+  float M[KC], den[KC];
+  f32x4_t num[KC];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) num[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < np; k0 += KB) {
-    float mk[KB], lk[KB];
-    f32x4_t ak[KB][NT];
+  for (int k = 0; k < KC; ++k) {
+    ch[k] = lane + 64 * k;
+    ok[k] = ch[k] < nchunk;
+    hd[k] = ok[k] ? (4 * ch[k]) / D : 0;
+    M[k] = -INFINITY;
+    den[k] = 0.f;
+    num[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < np; k0 += PPB) {
+    f32x4_t a[PPB][KC];
+    f32x2_t ml[PPB][KC];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const int k = min(k0 + j, np - 1);
-      const float* part = p.partials + ((int64_t)(w + k) * 2 + (k == 0 ? slot0 : 0)) * PF;
-      mk[j] = part[16 * D + 2 * lr];
-      lk[j] = part[16 * D + 2 * lr + 1];
+    for (int j = 0; j < PPB; ++j) {
+      const int pc = min(k0 + j, np - 1);
+      const float* part = p.partials + ((int64_t)(w + pc) * 2 + (pc == 0 ? slot0 : 0)) * PF;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        ak[j][nt] = *reinterpret_cast<const f32x4_t*>(part + lane * (4 * NT) + 4 * nt);
-    }
-    float mb = M;
-#pragma unroll
-    for (int j = 0; j < KB; ++j)
-      if (k0 + j < np) mb = fmaxf(mb, mk[j]);
-    const float base = mb == -INFINITY ? 0.f : mb;
-    const float sc = exp2_fast(M - base);
-    den *= sc;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) num[nt] *= sc;
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (k0 + j < np) {
-        const float f = exp2_fast(mk[j] - base);
-        den = __builtin_fmaf(f, lk[j], den);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) num[nt] += f * ak[j][nt];
+      for (int k = 0; k < KC; ++k) {
+        a[j][k] = ok[k] ? *reinterpret_cast<const f32x4_t*>(part + 4 * ch[k]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ml[j][k] = *reinterpret_cast<const f32x2_t*>(part + 16 * D + 2 * hd[k]);
       }
     }
-    M = mb;
-  }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  const int64_t row = ((int64_t)b * hkv * G + h * G + lr) * D;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int d = 16 * nt + 4 * lq;
-    if constexpr (IO_BF16) {
-      u32x2_t o;
-      o[0] = bf16_rne(num[nt][0] * inv) | (bf16_rne(num[nt][1] * inv) << 16);
-      o[1] = bf16_rne(num[nt][2] * inv) | (bf16_rne(num[nt][3] * inv) << 16);
-      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = o;
-    } else {
-      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = num[nt] * inv;
+    for (int k = 0; k < KC; ++k) {
+      float mb = M[k];
+#pragma unroll
+      for (int j = 0; j < PPB; ++j)
+        if (k0 + j < np) mb = fmaxf(mb, ml[j][k][0]);
+      const float base = mb == -INFINITY ? 0.f : mb;
+      const float sc = exp2_fast(M[k] - base);
+      den[k] *= sc;
+      num[k] *= sc;
+#pragma unroll
+      for (int j = 0; j < PPB; ++j) {
+        if (k0 + j < np) {
+          const float f = exp2_fast(ml[j][k][0] - base);
+          den[k] = __builtin_fmaf(f, ml[j][k][1], den[k]);
+          num[k] += f * a[j][k];
+        }
+      }
+      M[k] = mb;
     }
   }
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    if (!ok[k]) continue;
+    const float inv = den[k] > 0.f ? 1.0f / den[k] : 0.f;
+    const int d = 4 * ch[k] - hd[k] * D;
+    const int64_t row = ((int64_t)b * hkv * G + h * G + hd[k]) * D;
+    if constexpr (IO_BF16) {
+      u32x2_t o;
+      o[0] = bf16_rne(num[k][0] * inv) | (bf16_rne(num[k][1] * inv) << 16);
+      o[1] = bf16_rne(num[k][2] * inv) | (bf16_rne(num[k][3] * inv) << 16);
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = o;
+    } else {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = num[k] * inv;
+    }
+  }
+}
+
+// 16-byte chunks per lane the merge needs for G*D accumulators: a power of
+// two >= G*D / 256.
+template <bool IO_BF16, int D>
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
+  const int need = (p.group * D / 4 + 63) / 64;
+  const dim3 grid(p.n_waves / 4), block(kBlockThreads);
+  hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
+  if (need <= 1) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 1>), grid, block, 0, stream, e0, e1, 0, p);
+  else if (need <= 2) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 2>), grid, block, 0, stream, e0, e1, 0, p);
+  else if (need <= 4) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 4>), grid, block, 0, stream, e0, e1, 0, p);
+  else hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 8>), grid, block, 0, stream, e0, e1, 0, p);
+  return hipGetLastError();
 }
 
 template <int KV, int D, int BS>
@@ -1057,10 +1077,7 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
                         static_cast<char*>(p.k_pool), static_cast<char*>(p.v_pool));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipExtLaunchKernelGGL((decode_merge_kernel<KV != KV_F32, D>), dim3(p.n_waves / 4),
-                        dim3(kBlockThreads), 0, stream, ev ? ev[2] : nullptr,
-                        ev ? ev[3] : nullptr, 0, p);
-  return hipGetLastError();
+  return launch_merge<KV != KV_F32, D>(p, stream, ev);
 }
 
 template <int KV, int D, int BS>
