@@ -126,6 +126,20 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // instead of degrading to full drains on every path.
 __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Issue priority of the wavefront (0..3, uniform argument).  Two
+// wavefronts on one SIMD otherwise share its issue slots oldest-first, and
+// the older one streams its tiles much faster while both run.  Each
+// wavefront lowers its priority as it gets through its tiles (3 until half
+// done, 2 until 3/4, 1 until 7/8, then 0), so the one that is behind wins
+// the issue slots until it catches up: the two meet at each of those marks
+// and finish within about 1/8 of their tiles of each other.
+__device__ __forceinline__ void set_priority(int level) {
+  if (level >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (level == 2) __builtin_amdgcn_s_setprio(2);
+  else if (level == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // float32 -> bfloat16 bits, round to nearest even (finite), quiet NaN.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -915,6 +929,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   // buffer) so that the wait before each tile is a fixed count of the loads
   // issued after it.
   for (int base = 0; base < T; base += R) {
+    {
+      const int left8 = (8 * (T - base) + T - 1) / T;    // ceil(8 * tiles left / T)
+      set_priority(uniform(left8 > 4 ? 3 : left8 > 2 ? 2 : left8 > 1 ? 1 : 0));
+    }
     static_for([&](auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       const int i = base + u;
