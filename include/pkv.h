@@ -106,6 +106,7 @@ typedef struct pkv_pool_info {
   int32_t piece_cost;
   int32_t young_weight_pct;
   int32_t n_first;           /* wavefronts of the first workgroup on each CU */
+  int32_t odd_weight_pct;
 } pkv_pool_info;
 
 /* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
@@ -191,7 +192,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
 pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 
 /* Tuning knobs (also read from PKV_WAVES_PER_CU, PKV_MIN_UNITS,
- * PKV_PIECE_COST and PKV_YOUNG_WEIGHT at pool creation).  The step's work is
+ * PKV_PIECE_COST, PKV_YOUNG_WEIGHT and PKV_ODD_WEIGHT at pool creation).  The step's work is
  * measured in units: one per 16-token tile, plus piece_cost for starting
  * each (request, KV head) sequence (its query rotation and append stall the
  * wavefront's loads), and split over the wavefronts in proportion to their
@@ -210,10 +211,15 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
  *    while both run.  100 splits evenly.  The weights apply only to steps
  *    with at least 256 units per launched wavefront (below that start-up
  *    dominates and the split is even).
+ *  - odd_weight_pct: share weight of the wavefronts of odd workgroups, in
+ *    percent of the even ones' ([1, 100], or -1 for the default 90), on
+ *    top of the age weight and at every step size.  Workgroups are dealt to
+ *    the eight XCDs in turn, so odd workgroups run on odd XCDs, which stream
+ *    about a tenth slower on MI355X.  100 splits evenly.
  * Synchronises the device. */
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
                               int32_t min_units, int32_t piece_cost,
-                              int32_t young_weight_pct);
+                              int32_t young_weight_pct, int32_t odd_weight_pct);
 
 /* Measurement.  While enabled, decode_step launches its two kernels (the
  * fused attention kernel and the split-merge kernel) with HIP start/stop
@@ -255,18 +261,21 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
  * lengths clamped to [0, max_tokens]) and costs its tiles plus piece_cost
  * units; its tile 0 owns the units [s, s + piece_cost], tile j >= 1 the unit
  * s + piece_cost + j.  The sequences' units are concatenated in (request,
- * head) order, U in all.  If U >= weight_min_share * n_waves, wavefront w
- * weighs weight_first if w < n_first, else weight_rest (1 <= weight_rest <=
- * weight_first <= 1000); otherwise every wavefront weighs 1.  With Omega(w)
- * the summed weight of wavefronts [0, w), W active wavefronts split the
- * units at floor(U * Omega(w) / Omega(W)), and W is the largest value <=
- * n_waves (and >= 1) whose lightest wavefront still gets at least m =
- * max(min_units, piece_cost + 1) units: floor(U / m) if that is <= n_first,
- * else the largest W with U * weight_rest >= m * Omega(W) (but at least
- * n_first).  A wavefront takes the tiles whose first unit falls in its
- * range.  decode_step uses n_first = the first workgroup on each compute
- * unit (4 wavefronts per CU), weight_first = 100, weight_rest =
- * young_weight_pct and weight_min_share = 256.  Writes up to max_pieces rows of 6 int32 to pieces:
+ * head) order, U in all.  Wavefront w weighs a * p: its age weight a is
+ * weight_first if w < n_first, else weight_rest (1 <= weight_rest <=
+ * weight_first <= 1000), when U >= weight_min_share * n_waves, and 1
+ * otherwise; its parity weight p is weight_odd (in [1, 100]) if its
+ * workgroup w / 4 is odd, else 100.  With Omega(w) the summed weight of
+ * wavefronts [0, w), W active wavefronts split the units at
+ * floor(U * Omega(w) / Omega(W)), and W is the largest value <= n_waves (and
+ * >= 1) with U * a_min * p_min >= m * Omega(W), where m = max(min_units,
+ * piece_cost + 1) and a_min * p_min is the lightest weight any of the
+ * n_waves wavefronts has: every active wavefront gets at least m units.  A
+ * wavefront takes the tiles whose first unit falls in its range.
+ * decode_step uses n_first = the first workgroup on each compute unit (4
+ * wavefronts per CU), weight_first = 100, weight_rest = young_weight_pct,
+ * weight_odd = odd_weight_pct and weight_min_share = 256.  Writes up to
+ * max_pieces rows of 6 int32 to pieces:
  * {wave, request, kv_head, first_tile, end_tile, flags} with flags bit 0 =
  * the piece is part of a split sequence, bit 1 = it is the wave's first
  * piece, bit 2 = it is the last piece of its sequence; and n_waves rows of
@@ -276,7 +285,7 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
                          int32_t n_kv_heads, int32_t max_tokens, int32_t n_waves,
                          int32_t min_units, int32_t piece_cost, int32_t n_first,
-                         int32_t weight_first, int32_t weight_rest,
+                         int32_t weight_first, int32_t weight_rest, int32_t weight_odd,
                          int32_t weight_min_share, int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
                          int32_t* splits);
 

@@ -60,6 +60,7 @@ class _Info(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("ring_tiles", ctypes.c_int32),
         ("min_units", ctypes.c_int32), ("piece_cost", ctypes.c_int32),
         ("young_weight_pct", ctypes.c_int32), ("n_first", ctypes.c_int32),
+        ("odd_weight_pct", ctypes.c_int32),
     ]
 
 
@@ -85,7 +86,7 @@ def load_library(path: str = LIB_PATH):
         "kv_pool_get_info": (I32, [P, ctypes.POINTER(_Info)]),
         "decode_step": (I32, [P, P, P, P, I32, P, P, I32, P, I32, I32, P, P]),
         "kv_pool_device_errors": (I32, [P, ctypes.POINTER(ctypes.c_uint32)]),
-        "kv_pool_set_tuning": (I32, [P, I32, I32, I32, I32]),
+        "kv_pool_set_tuning": (I32, [P, I32, I32, I32, I32, I32]),
         "kv_pool_enable_timing": (I32, [P, I32]),
         "kv_pool_read_timing": (I32, [P, ctypes.POINTER(D), ctypes.POINTER(D),
                                       ctypes.POINTER(I32)]),
@@ -93,7 +94,7 @@ def load_library(path: str = LIB_PATH):
         "pkv_check_decode_args": (I32, [I64, I32, I32, I32, I32, I32, P, P, P, P, P,
                                         I32, P, I32, I32, P]),
         "pkv_rope_table_host": (I32, [D, I32, I32, FP, FP]),
-        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
+        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
         "pkv_tile_tokens": (I32, []),
     }
     for name, (res, args) in sig.items():
@@ -155,9 +156,10 @@ class KVPool:
         _check(_lib.kv_pool_set_fp8_scales(self.handle, ks, vs))
 
     def set_tuning(self, waves_per_cu: int = 0, min_units: int = 16, piece_cost: int = -1,
-                   young_weight_pct: int = -1) -> None:
+                   young_weight_pct: int = -1, odd_weight_pct: int = -1) -> None:
         _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_units),
-                                       int(piece_cost), int(young_weight_pct)))
+                                       int(piece_cost), int(young_weight_pct),
+                                       int(odd_weight_pct)))
 
     def enable_timing(self, enable: bool = True) -> None:
         _check(_lib.kv_pool_enable_timing(self.handle, 1 if enable else 0))
@@ -297,12 +299,14 @@ def rope_table_host(theta: float, head_dim: int, max_position: int):
 
 def plan_host(context_lens, n_kv_heads: int, max_tokens: int, n_waves: int,
               min_units: int, piece_cost: int = 0, n_first: int = 0, weight_first: int = 1,
-              weight_rest: int = 1, weight_min_share: int = 0, max_pieces: int = 1 << 20):
+              weight_rest: int = 1, weight_min_share: int = 0, max_pieces: int = 1 << 20,
+              weight_odd: int = 100):
     """Host replay of the kernel's work partition (numpy arrays): pieces
     ``[n, 6]`` and the per-wave split-sequence rows ``[n_waves, 4]``.  The
     first ``n_first`` wavefronts weigh ``weight_first``, the rest
     ``weight_rest``, when there are at least ``weight_min_share`` units per
-    wavefront (else, and with equal weights, the split is even)."""
+    wavefront (else those age weights are even); wavefronts of odd
+    workgroups (index // 4 odd) are further weighted ``weight_odd`` percent."""
     import numpy as np
 
     lib = load_library()
@@ -313,7 +317,7 @@ def plan_host(context_lens, n_kv_heads: int, max_tokens: int, n_waves: int,
     ip = ctypes.POINTER(ctypes.c_int32)
     _check(lib.pkv_plan_host(lens.ctypes.data_as(ip), int(lens.shape[0]), int(n_kv_heads),
                              int(max_tokens), int(n_waves), int(min_units), int(piece_cost),
-                             int(n_first), int(weight_first), int(weight_rest),
+                             int(n_first), int(weight_first), int(weight_rest), int(weight_odd),
                              int(weight_min_share), int(max_pieces),
                              pieces.ctypes.data_as(ip), ctypes.byref(n),
                              splits.ctypes.data_as(ip)))

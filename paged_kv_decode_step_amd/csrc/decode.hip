@@ -389,7 +389,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 
   const int64_t U = sP[B];                               // work units
   const WaveWeights ww = weights_for(U, p.n_waves, p.weight_min_share,
-                                     WaveWeights{p.weight_first, p.weight_rest, p.n_first});
+                                     WaveWeights{p.weight_first, p.weight_rest, p.n_first, p.weight_odd});
   const int64_t W = active_waves(U, p.n_waves, p.min_units, ww);
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
   if (wave >= W) {

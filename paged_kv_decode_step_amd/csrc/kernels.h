@@ -46,6 +46,7 @@ struct DecodeParams {
   int32_t n_first;           // wavefronts of the first workgroup on each compute unit
   int32_t weight_first;      // their share weight ...
   int32_t weight_rest;       // ... and that of the others (weight_first >= weight_rest >= 1)
+  int32_t weight_odd;        // parity weight of odd workgroups, percent of even ones' (1..100)
   int32_t weight_min_share;  // units per wavefront below which the weights are even
   float sm_scale_log2;       // log2(e) / sqrt(D)
 };

@@ -70,6 +70,14 @@ int resolve_young_pct(int requested) {
   return std::max(1, std::min(v, 100));
 }
 
+// Share weight of the wavefronts of odd workgroups, in percent of the even
+// ones'.  Workgroups are dealt to the eight XCDs in turn, and the odd XCDs
+// were measured to stream about a tenth slower; -1 asks for 90%.
+int resolve_odd_pct(int requested) {
+  const int v = requested < 0 ? 90 : requested;
+  return std::max(1, std::min(v, 100));
+}
+
 }  // namespace
 
 struct pkv_pool {
@@ -99,6 +107,7 @@ struct pkv_pool {
   int piece_cost = 0;       // resolved (never the automatic -1)
   int ring_tiles = 0;
   int young_pct = 100;      // share weight of later workgroups, % of the first's
+  int odd_pct = 100;        // share weight of odd workgroups, % of the even ones'
   // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -220,6 +229,7 @@ pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_h
   p->ring_tiles = pkv::decode_ring_tiles(kv_kind(kv_dtype), head_dim);
   p->piece_cost = resolve_piece_cost(env_int("PKV_PIECE_COST", -1), p->ring_tiles);
   p->young_pct = resolve_young_pct(env_int("PKV_YOUNG_WEIGHT", -1));
+  p->odd_pct = resolve_odd_pct(env_int("PKV_ODD_WEIGHT", -1));
   pkv_status s = size_workspace(p, env_int("PKV_WAVES_PER_CU", 0));
   if (s != PKV_OK) { free_pool(p); return s; }
   *out_pool = p;
@@ -310,12 +320,14 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->min_units = pool->min_units;
   info->piece_cost = pool->piece_cost;
   info->young_weight_pct = pool->young_pct;
+  info->odd_weight_pct = pool->odd_pct;
   info->n_first = std::min(pool->n_waves, 4 * pool->cus);
   return PKV_OK;
 }
 
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_units,
-                              int32_t piece_cost, int32_t young_weight_pct) {
+                              int32_t piece_cost, int32_t young_weight_pct,
+                              int32_t odd_weight_pct) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
   if (min_units < 1) return fail(PKV_ERR_INVALID, "min_units must be >= 1");
   if (piece_cost < -1 || piece_cost > pkv::kMaxPieceCost)
@@ -323,6 +335,8 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
                 pkv::kMaxPieceCost);
   if (young_weight_pct < -1 || young_weight_pct == 0 || young_weight_pct > 100)
     return fail(PKV_ERR_INVALID, "young_weight_pct must be -1 (automatic) or in [1, 100]");
+  if (odd_weight_pct < -1 || odd_weight_pct == 0 || odd_weight_pct > 100)
+    return fail(PKV_ERR_INVALID, "odd_weight_pct must be -1 (automatic) or in [1, 100]");
   if (waves_per_cu < 0 || waves_per_cu > 32)
     return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
   int cur = 0;
@@ -335,6 +349,7 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
   pool->min_units = min_units;
   pool->piece_cost = resolve_piece_cost(piece_cost, pool->ring_tiles);
   pool->young_pct = resolve_young_pct(young_weight_pct);
+  pool->odd_pct = resolve_odd_pct(odd_weight_pct);
   return PKV_OK;
 }
 
@@ -480,6 +495,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.n_first = std::min(pool->n_waves, 4 * pool->cus);
   p.weight_first = 100;
   p.weight_rest = pool->young_pct;
+  p.weight_odd = pool->odd_pct;
   p.weight_min_share = pkv::kWeightMinShare;
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   hipEvent_t* ev = nullptr;
@@ -543,7 +559,7 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
 pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
                          int32_t max_tokens, int32_t n_waves, int32_t min_units,
                          int32_t piece_cost, int32_t n_first, int32_t weight_first,
-                         int32_t weight_rest, int32_t weight_min_share,
+                         int32_t weight_rest, int32_t weight_odd, int32_t weight_min_share,
                          int32_t max_pieces, int32_t* pieces,
                          int32_t* n_pieces, int32_t* splits) {
   if (!context_lens || !n_pieces || !splits || (max_pieces > 0 && !pieces))
@@ -554,6 +570,7 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
     return fail(PKV_ERR_INVALID, "piece_cost must be in [0, %d]", pkv::kMaxPieceCost);
   if (n_first < 0 || weight_rest < 1 || weight_first < weight_rest || weight_first > 1000)
     return fail(PKV_ERR_INVALID, "need n_first >= 0 and 1 <= weight_rest <= weight_first <= 1000");
+  if (weight_odd < 1 || weight_odd > 100) return fail(PKV_ERR_INVALID, "weight_odd must be in [1, 100]");
   if (weight_min_share < 0) return fail(PKV_ERR_INVALID, "weight_min_share must be >= 0");
   const int hkv = n_kv_heads, cost = piece_cost;
   std::vector<int> P(batch + 1, 0);
@@ -561,7 +578,7 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
     P[b + 1] = P[b] + hkv * (pkv::tiles_of(context_lens[b], max_tokens) + cost);
   const int64_t C = P[batch];
   const pkv::WaveWeights ww = pkv::weights_for(
-      C, n_waves, weight_min_share, pkv::WaveWeights{weight_first, weight_rest, n_first});
+      C, n_waves, weight_min_share, pkv::WaveWeights{weight_first, weight_rest, n_first, weight_odd});
   const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1), ww);
   const int64_t n_tiles = (int64_t)P[batch] - (int64_t)hkv * cost * batch;
   for (int64_t w = 0; w < n_waves; ++w) {

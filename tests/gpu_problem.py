@@ -56,6 +56,7 @@ class Run:
 
     def __init__(self, wl: workloads.Workload, arrs: dict, *, waves_per_cu: int = 0,
                  min_units: int = None, piece_cost: int = None, young_weight: int = None,
+                 odd_weight: int = None,
                  max_position: int = None, tables=None):
         c = wl.cfg
         self.wl, self.arrs = wl, arrs
@@ -64,10 +65,12 @@ class Run:
         self.pool.set_rope(c.rope_theta, max_position or max(wl.max_position, 1))
         if c.kv_dtype == "fp8":
             self.pool.set_fp8_scales(arrs["k_scale"], arrs["v_scale"])
-        if waves_per_cu or min_units or piece_cost is not None or young_weight is not None:
+        if (waves_per_cu or min_units or piece_cost is not None or young_weight is not None
+                or odd_weight is not None):
             self.pool.set_tuning(waves_per_cu, min_units or 16,
                                  -1 if piece_cost is None else piece_cost,
-                                 -1 if young_weight is None else young_weight)
+                                 -1 if young_weight is None else young_weight,
+                                 -1 if odd_weight is None else odd_weight)
         pool_io.write_logical(self.pool, codes_to_torch(arrs["k_pool"], c.kv_dtype),
                               codes_to_torch(arrs["v_pool"], c.kv_dtype))
         self.q = io_to_torch(arrs["q"], c.io_dtype)

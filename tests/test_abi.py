@@ -101,12 +101,13 @@ def test_tile_tokens():
 
 # ---- work partition ---------------------------------------------------------
 def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=1, wr=1,
-                        min_share=0):
+                        min_share=0, wo=100):
     """The partition written out plainly: sequences (b, h) in order, each cut
     into max(1, ceil(min(L, cap)/16)) tiles and costing its tiles plus
-    `cost` units (tile 0 owns cost + 1 units); wave w weighs wf if
-    w < n_first else wr; the most waves whose every member's exact share
-    is >= max(min_units, cost + 1) units are used (found by trying every
+    `cost` units (tile 0 owns cost + 1 units); wave w weighs (wf if
+    w < n_first else wr) * (wo if (w // 4) is odd else 100); the most waves
+    whose exact share for a wave of the lightest of all n_waves weights is
+    >= max(min_units, cost + 1) units are used (found by trying every
     count); the units are cut at floor(total * weights before w / all
     weights) and each tile is owned by the wave holding its first unit."""
     ns = [max(1, -(-min(max(int(L), 0), cap) // 16)) for L in lens]
@@ -121,11 +122,12 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
     m = max(min_units, cost + 1)
     if total < min_share * n_waves:     # too little work per wave: even weights
         wf = wr = 1
-    weight = [wf if w < n_first else wr for w in range(n_waves)]
+    weight = [(wf if w < n_first else wr) * (wo if (w // 4) % 2 else 100)
+              for w in range(n_waves)]
+    lightest = min(weight)
 
     def enough(count):
-        om = sum(weight[:count])
-        return all(total * weight[w] >= m * om for w in range(count))
+        return total * lightest >= m * sum(weight[:count])
 
     we = max([c for c in range(1, n_waves + 1) if enough(c)], default=1)
     om = sum(weight[:we])
@@ -163,13 +165,14 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
     ([23, 10], 2, 64, 6, 5, 0, 1, 1),         # ceil(U/m) = 5 waves would leave wave 3 no tile
 ])
 @pytest.mark.parametrize("min_share", [0, 40])
+@pytest.mark.parametrize("wo", [100, 90, 37, 1])
 def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_units, cost,
-                                                       nf, wf, wr, min_share):
+                                                       nf, wf, wr, min_share, wo):
     cap = 1 << 20
     pieces, splits = pkv.plan_host(lens, hkv, cap, waves, min_units, cost, nf, wf, wr,
-                                   min_share)
+                                   min_share, weight_odd=wo)
     owner, bounds, we, seqs = reference_partition(lens, hkv, cap, waves, min_units, cost,
-                                                  nf, wf, wr, min_share)
+                                                  nf, wf, wr, min_share, wo)
     if bounds[-1] < min_share * waves:
         wf = wr = 1
     seen = {}
@@ -184,7 +187,8 @@ def test_partition_covers_every_tile_once_and_balances(lens, hkv, waves, min_uni
     # every active wave owns a tile; unit ranges within one of their exact shares
     assert np.all(per_wave[:we] >= 1) and np.all(per_wave[we:] == 0)
     sizes = np.diff(bounds)
-    weights = np.array([wf if w < nf else wr for w in range(we)], dtype=np.float64)
+    weights = np.array([(wf if w < nf else wr) * (wo if (w // 4) % 2 else 100)
+                        for w in range(we)], dtype=np.float64)
     exact = bounds[-1] * weights / weights.sum()
     assert np.all(np.abs(sizes - exact) < 1.0)
     # flags and split rows against a direct reading

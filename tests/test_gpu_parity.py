@@ -97,8 +97,11 @@ def test_many_splits_and_no_split_agree(kv):
     out_d, _, _ = run_and_check(wl, arrs, waves_per_cu=8, min_units=1, piece_cost=0,
                                 young_weight=1)
     out_e, _, _ = run_and_check(wl, arrs, waves_per_cu=12, min_units=1, piece_cost=2,
-                                young_weight=100)
-    for other in (out_b, out_c, out_d, out_e):
+                                young_weight=100, odd_weight=100)
+    # odd workgroups weighted down to almost nothing, on top of the age weights
+    out_f, _, _ = run_and_check(wl, arrs, waves_per_cu=8, min_units=1, piece_cost=3,
+                                young_weight=40, odd_weight=1)
+    for other in (out_b, out_c, out_d, out_e, out_f):
         assert gp.row_rel_err(out_a, other).max() <= gp.tolerance(kv)
 
 
