@@ -44,7 +44,8 @@ typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID = -1,      /* bad argument (null, out of range, mismatch) */
   PKV_ERR_UNSUPPORTED = -2,  /* valid but not built (dtype/size combination) */
-  PKV_ERR_OOM = -3,          /* device allocation failed */
+  PKV_ERR_OOM = -3,          /* device allocation failed, or the block
+                                allocator is out of blocks or sequence ids */
   PKV_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
   PKV_ERR_STATE = -5,        /* call order (e.g. no RoPE table set yet) */
   PKV_ERR_DEVICE_DATA = -6   /* device-resident arguments out of range */
@@ -221,6 +222,20 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
                               int32_t min_units, int32_t piece_cost,
                               int32_t young_weight_pct, int32_t odd_weight_pct);
 
+/* Copy whole blocks inside the pool: for i < n_pairs, block pairs[2i + 1]
+ * gets the K and V contents (every head and slot) of block pairs[2i].  This
+ * is the copy on write of a shared prefix block, done before a step appends
+ * to it (pkv_alloc_prepare_step names the pairs); blocks reused across
+ * requests that share a prefix: "Lesson 13.17 TensorRT-LLM: NVIDIA's
+ * Optimized Inference Engine", section "The paged KV cache, in-flight
+ * batching and CUDA graphs".  pairs: device int32 [n_pairs][2], owned by the
+ * caller, valid until the copy has run on `stream`; no destination may also
+ * be a source or appear twice (the copies run in any order).  Asynchronous on
+ * `stream` (a hipStream_t; NULL = the default stream).  Ids outside [0, num_blocks) are skipped and reported as flag 1
+ * of kv_pool_device_errors; a pair with equal ids does nothing. */
+pkv_status kv_pool_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs,
+                               void* stream);
+
 /* Measurement.  While enabled, decode_step launches its two kernels (the
  * fused attention kernel and the split-merge kernel) with HIP start/stop
  * events that the dispatches themselves stamp.  kv_pool_read_timing waits
@@ -234,6 +249,77 @@ pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* pkv_last_error(void);
+
+/* ---- block allocator (host only, no GPU needed) --------------------------
+ *
+ * The cache lives in fixed-size blocks handed out on demand as tokens are
+ * generated, with waste bounded by each sequence's last, partly filled block
+ * ("TensorRT-LLM Guide: High-Throughput GPU Inference Engine", section
+ * "2. Paged KV Cache & Memory Virtualization"); the scheduler updates the
+ * block tables every iteration ("Scaling TensorRT-LLM: Kernel Fusion and
+ * Inflight Batching in Production", section "What the Scheduler Actually
+ * Does"); blocks are reused across requests that share a prefix ("Lesson
+ * 13.17 TensorRT-LLM: NVIDIA's Optimized Inference Engine", section "The
+ * paged KV cache, in-flight batching and CUDA graphs").
+ *
+ * A sequence holds a list of block ids and a length in tokens.  A block
+ * carries a reference count: the number of sequences holding it.  Free blocks
+ * sit on a stack: a new allocator hands out 0, 1, 2, ..., and the most
+ * recently freed block is the next one handed out.  Sequence ids are the
+ * lowest free id.  Not thread-safe; it never touches the GPU.  Every call
+ * that fails leaves the allocator unchanged. */
+typedef struct pkv_block_alloc pkv_block_alloc;
+
+/* An allocator over num_blocks blocks of block_size tokens and at most
+ * max_seqs live sequences.  PKV_ERR_INVALID for sizes < 1. */
+pkv_status pkv_alloc_create(int64_t num_blocks, int32_t block_size, int32_t max_seqs,
+                            pkv_block_alloc** out);
+pkv_status pkv_alloc_destroy(pkv_block_alloc* alloc);
+
+/* Free blocks and live sequences (either pointer may be NULL). */
+pkv_status pkv_alloc_stats(const pkv_block_alloc* alloc, int64_t* free_blocks,
+                           int32_t* live_seqs);
+
+/* Reference count of one block (0 = free). */
+pkv_status pkv_alloc_refcount(const pkv_block_alloc* alloc, int32_t block, int32_t* count);
+
+/* A new sequence already holding `length` tokens (a prompt whose K/V the
+ * caller writes into its blocks): ceil(length / block_size) fresh blocks.
+ * PKV_ERR_OOM if the blocks or a sequence id are not available. */
+pkv_status pkv_seq_add(pkv_block_alloc* alloc, int32_t length, int32_t* seq);
+
+/* A new sequence sharing every block of `parent` (prefix sharing: parallel
+ * samples, beams, a common system prompt); same length; each shared block's
+ * count goes up by one. */
+pkv_status pkv_seq_fork(pkv_block_alloc* alloc, int32_t parent, int32_t* child);
+
+/* End a sequence: each of its blocks' counts goes down by one, and blocks
+ * that reach zero are freed (its last block first). */
+pkv_status pkv_seq_release(pkv_block_alloc* alloc, int32_t seq);
+
+/* Length, block count and the first min(max_blocks, count) block ids. */
+pkv_status pkv_seq_info(const pkv_block_alloc* alloc, int32_t seq, int32_t* length,
+                        int32_t* n_blocks, int32_t* blocks, int32_t max_blocks);
+
+/* The host side of one decode step for the batch seq_ids[0 .. batch): each
+ * sequence (distinct ids) grows by the step's new token, at slot = its old
+ * length.  If the slot starts a block, a fresh block is appended; if the
+ * block holding the slot is shared, the sequence gets a fresh block in its
+ * place and the pair {shared, fresh} goes to `copies` (copy on write; when
+ * every holder of a shared block appends in the same step, the last of them
+ * in batch order keeps it).  Writes, in host memory the caller owns, the
+ * arguments decode_step takes: block_tables [batch][max_blocks_per_seq]
+ * (ids, then -1), context_lens [batch] (the new lengths, counting the new
+ * token) and positions [batch] (new length - 1), plus up to max_copies pairs
+ * to copies [max_copies][2] and their number to *n_copies.  The caller runs
+ * kv_pool_copy_blocks on the pairs before decode_step.  PKV_ERR_INVALID for a
+ * dead or repeated id, a sequence outgrowing max_blocks_per_seq blocks or more
+ * copies than max_copies; PKV_ERR_OOM if the free blocks do not cover the
+ * fresh blocks and copies. */
+pkv_status pkv_alloc_prepare_step(pkv_block_alloc* alloc, const int32_t* seq_ids, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t* block_tables,
+                                  int32_t* context_lens, int32_t* positions, int32_t* copies,
+                                  int32_t max_copies, int32_t* n_copies);
 
 /* ---- host-only helpers (no GPU needed) --------------------------------- */
 

@@ -32,7 +32,11 @@ casts; RoPE against closed forms and the relative-position identity;
 attention against closed forms (one token, identical keys, zero query),
 linearity, block-permutation invariance, a padded static batch computed on a
 separate dense path, ``scaled_dot_product_attention`` in float64 and an
-mpmath brute force on tiny inputs.  No function here is "parity unpinned".
+mpmath brute force on tiny inputs; the dense-history steps against
+``decode_step`` on paged layouts of the same histories; the allocator
+against its invariants (reference counts equal the holders, blocks conserved,
+an appending sequence's block exclusive) and a token-level simulation of the
+pool.  No function here is "parity unpinned".
 """
 from .codecs import (bf16_bits_from_f32, bf16_bits_to_f32, bf16_bits_to_f64,
                      fp8_code_value, fp8_encode, fp8_decode, FP8_MAX)
@@ -42,6 +46,8 @@ from .decode import (decode_step, gather_request, attention_request,
                      cast_to_kv)
 from .variants import (padded_static_batch, split_merge,
                        brute_force_rotate_key, brute_force_attention)
+from .block_alloc import BlockAllocator, AllocError
+from .history import DenseHistories
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f32", "bf16_bits_to_f64",
@@ -50,5 +56,5 @@ __all__ = [
     "decode_step", "gather_request", "attention_request", "io_to_f64",
     "io_to_f32", "kv_to_f64", "fp8_inverse_scale", "cast_to_kv",
     "padded_static_batch", "split_merge", "brute_force_rotate_key",
-    "brute_force_attention",
+    "brute_force_attention", "BlockAllocator", "AllocError", "DenseHistories",
 ]

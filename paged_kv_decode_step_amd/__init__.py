@@ -19,7 +19,7 @@ import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
 __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "BlockAllocator",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -36,7 +36,10 @@ EXPORTED_SYMBOLS = (
     "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
     "kv_pool_read_timing", "pkv_last_error",
     "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
-    "pkv_tile_tokens",
+    "pkv_tile_tokens", "kv_pool_copy_blocks",
+    "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
+    "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
+    "pkv_alloc_prepare_step",
 )
 
 
@@ -96,6 +99,16 @@ def load_library(path: str = LIB_PATH):
         "pkv_rope_table_host": (I32, [D, I32, I32, FP, FP]),
         "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
         "pkv_tile_tokens": (I32, []),
+        "kv_pool_copy_blocks": (I32, [P, P, I32, P]),
+        "pkv_alloc_create": (I32, [I64, I32, I32, ctypes.POINTER(P)]),
+        "pkv_alloc_destroy": (I32, [P]),
+        "pkv_alloc_stats": (I32, [P, ctypes.POINTER(I64), IP]),
+        "pkv_alloc_refcount": (I32, [P, I32, IP]),
+        "pkv_seq_add": (I32, [P, I32, IP]),
+        "pkv_seq_fork": (I32, [P, I32, IP]),
+        "pkv_seq_release": (I32, [P, I32]),
+        "pkv_seq_info": (I32, [P, I32, IP, IP, IP, I32]),
+        "pkv_alloc_prepare_step": (I32, [P, IP, I32, I32, IP, IP, IP, IP, I32, IP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -160,6 +173,20 @@ class KVPool:
         _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_units),
                                        int(piece_cost), int(young_weight_pct),
                                        int(odd_weight_pct)))
+
+    def copy_blocks(self, pairs, stream=None) -> None:
+        """Copy whole blocks, ``pairs`` an int32 ``[n, 2]`` device tensor of
+        (source, destination) ids (``kv_pool_copy_blocks``; asynchronous)."""
+        if pairs.dtype != torch.int32 or not pairs.is_contiguous() or pairs.device.type != "cuda":
+            raise PkvError(-1, "pairs must be a contiguous int32 GPU tensor")
+        if pairs.dim() != 2 or pairs.shape[1] != 2:
+            raise PkvError(-1, "pairs must be [n, 2]")
+        if stream is None:
+            stream = torch.cuda.current_stream(pairs.device).cuda_stream
+        elif not isinstance(stream, int):
+            stream = stream.cuda_stream
+        _check(_lib.kv_pool_copy_blocks(self.handle, _ptr(pairs), int(pairs.shape[0]),
+                                        ctypes.c_void_p(stream)))
 
     def enable_timing(self, enable: bool = True) -> None:
         _check(_lib.kv_pool_enable_timing(self.handle, 1 if enable else 0))
@@ -257,6 +284,95 @@ def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
                            _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
                            _ptr(context_lens), batch, hq, _ptr(out),
                            ctypes.c_void_p(stream)))
+
+
+class BlockAllocator:
+    """Host block allocator of a paged pool (``pkv_alloc_*`` / ``pkv_seq_*``):
+    sequences hold block lists, shared blocks are reference counted, and
+    ``prepare_step`` returns a step's block tables, lengths, positions and
+    the copy-on-write pairs as numpy arrays."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.pkv_alloc_create(int(num_blocks), int(block_size), int(max_seqs),
+                                    ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size, self.max_seqs = int(num_blocks), int(block_size), int(max_seqs)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise PkvError(-5, "allocator is closed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h is not None:
+            _lib.pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stats(self):
+        """(free blocks, live sequences)."""
+        fb, ls = ctypes.c_int64(), ctypes.c_int32()
+        _check(_lib.pkv_alloc_stats(self.handle, ctypes.byref(fb), ctypes.byref(ls)))
+        return fb.value, ls.value
+
+    def refcount(self, block: int) -> int:
+        c = ctypes.c_int32()
+        _check(_lib.pkv_alloc_refcount(self.handle, int(block), ctypes.byref(c)))
+        return c.value
+
+    def add(self, length: int) -> int:
+        s = ctypes.c_int32()
+        _check(_lib.pkv_seq_add(self.handle, int(length), ctypes.byref(s)))
+        return s.value
+
+    def fork(self, parent: int) -> int:
+        s = ctypes.c_int32()
+        _check(_lib.pkv_seq_fork(self.handle, int(parent), ctypes.byref(s)))
+        return s.value
+
+    def release(self, seq: int) -> None:
+        _check(_lib.pkv_seq_release(self.handle, int(seq)))
+
+    def info(self, seq: int):
+        """(length, block ids as a list)."""
+        import numpy as np
+
+        length, nb = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pkv_seq_info(self.handle, int(seq), ctypes.byref(length), ctypes.byref(nb),
+                                 None, 0))
+        blocks = np.zeros(max(nb.value, 1), dtype=np.int32)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        _check(_lib.pkv_seq_info(self.handle, int(seq), None, None, blocks.ctypes.data_as(ip),
+                                 nb.value))
+        return length.value, [int(b) for b in blocks[:nb.value]]
+
+    def prepare_step(self, seq_ids, max_blocks_per_seq: int, max_copies: int = None):
+        """Grow each sequence by one token: (block_tables [B, max_blocks_per_seq],
+        context_lens [B], positions [B], copies [n, 2]), int32 numpy arrays."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        b = int(ids.shape[0])
+        mc = b if max_copies is None else int(max_copies)
+        tables = np.zeros((max(b, 1), int(max_blocks_per_seq)), dtype=np.int32)
+        lens = np.zeros(max(b, 1), dtype=np.int32)
+        pos = np.zeros(max(b, 1), dtype=np.int32)
+        copies = np.zeros((max(mc, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        ip = ctypes.POINTER(ctypes.c_int32)
+        _check(_lib.pkv_alloc_prepare_step(self.handle, ids.ctypes.data_as(ip), b,
+                                           int(max_blocks_per_seq), tables.ctypes.data_as(ip),
+                                           lens.ctypes.data_as(ip), pos.ctypes.data_as(ip),
+                                           copies.ctypes.data_as(ip), mc, ctypes.byref(n)))
+        return tables[:b], lens[:b], pos[:b], copies[:n.value]
 
 
 # ---- host-only helpers -----------------------------------------------------

@@ -14,7 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = [os.path.join(HERE, "csrc", "decode.hip"),
-           os.path.join(HERE, "csrc", "pkv_host.cpp")]
+           os.path.join(HERE, "csrc", "blocks.hip"),
+           os.path.join(HERE, "csrc", "pkv_host.cpp"),
+           os.path.join(HERE, "csrc", "block_alloc.cpp")]
 
 
 def hipcc() -> str:

@@ -66,6 +66,13 @@ int decode_ring_tiles(int kv_kind, int head_dim);
 // Resident 256-thread workgroups per compute unit for the attention kernel.
 hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks_per_cu);
 
+// Copy n whole blocks of the pool, K and V, from pairs[2i] to pairs[2i + 1]
+// (device int32 pairs; block_bytes per block of K, a multiple of 16).  Ids
+// outside [0, num_blocks) set err[0] and are skipped.
+hipError_t launch_copy_blocks(const int32_t* pairs, int32_t n, int64_t block_bytes,
+                              int32_t num_blocks, void* k_pool, void* v_pool, uint32_t* err,
+                              hipStream_t stream);
+
 // Bytes of workspace the kernels need for n_waves wavefronts (partials).
 inline size_t partials_bytes(int n_waves, int head_dim) {
   return (size_t)n_waves * 2 * partial_floats(head_dim) * sizeof(float);

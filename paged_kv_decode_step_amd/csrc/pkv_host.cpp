@@ -80,6 +80,14 @@ int resolve_odd_pct(int requested) {
 
 }  // namespace
 
+namespace pkv {
+// The thread-local error message, for the other host sources of the library.
+pkv_status set_error(pkv_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+}  // namespace pkv
+
 struct pkv_pool {
   int device = 0;
   int64_t num_blocks = 0;
@@ -513,6 +521,19 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   hipError_t e = pkv::launch_decode(kv_kind(pool->kv_dtype), pool->head_dim, pool->block_size, p,
                                     st, ev);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return PKV_OK;
+}
+
+pkv_status kv_pool_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs,
+                               void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (n_pairs < 0) return fail(PKV_ERR_INVALID, "n_pairs must be >= 0");
+  if (n_pairs == 0) return PKV_OK;
+  if (!pairs) return fail(PKV_ERR_INVALID, "pairs is null");
+  const hipError_t e = pkv::launch_copy_blocks(pairs, n_pairs, pool->kv_bytes / pool->num_blocks,
+                                               (int32_t)pool->num_blocks, pool->k, pool->v,
+                                               pool->err, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block copy launch");
   return PKV_OK;
 }
 
