@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the multi-layer step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run --steps plain device copies of 1 GiB (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -299,6 +301,32 @@ def main():
     attn_avg = attn_ms / max(calls, 1)
     merge_avg = merge_ms / max(calls, 1)
 
+    # the same steps replayed from one HIP graph that records a step on every
+    # pool copy: a multi-layer decode step issued with a single launch
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_layers):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_layers):
+                step(i)
+        reps = max(1, args.steps // n_layers)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / (reps * n_layers)
+        del graph
+
     gbs = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (attn_avg * 1e-3) / 1e9
     traffic = measured_traffic(c.name, alg)
@@ -324,6 +352,11 @@ def main():
         "tokens_per_s_per_layer": round(wl.batch / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,
         "kernel_ms": {"attention": round(attn_avg, 5), "merge": round(merge_avg, 5)},
+        "graph": None if graph_ms is None else {
+            "layers": n_layers, "ms_per_step": round(graph_ms, 5),
+            "GB/s": round(alg / (graph_ms * 1e-3) / 1e9, 2),
+            "note": "one HIP graph replays a step on each pool copy (a multi-layer step); "
+                    "value above is from eager launches"},
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
