@@ -108,6 +108,7 @@ typedef struct pkv_pool_info {
   int32_t young_weight_pct;
   int32_t n_first;           /* wavefronts of the first workgroup on each CU */
   int32_t odd_weight_pct;
+  int32_t window;            /* attention window in tokens, 0 = none */
 } pkv_pool_info;
 
 /* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
@@ -221,6 +222,15 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
 pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu,
                               int32_t min_units, int32_t piece_cost,
                               int32_t young_weight_pct, int32_t odd_weight_pct);
+
+/* Sliding-window attention for the pool's layer ("TensorRT-LLM" glossary
+ * entry, inferensys.com, which names Sliding Window Attention among the
+ * architecture patterns the kernels exploit): with window >= 1, each request
+ * of a later decode_step attends to its last `window` tokens only, the new
+ * one included, i.e. the tokens [max(0, L - window), L); whole blocks before
+ * the window are not read.  0 (the default) attends to the whole context.
+ * The append is unchanged.  PKV_ERR_INVALID for window < 0. */
+pkv_status kv_pool_set_window(pkv_pool* pool, int32_t window);
 
 /* Copy whole blocks inside the pool: for i < n_pairs, block pairs[2i + 1]
  * gets the K and V contents (every head and slot) of block pairs[2i].  This
@@ -358,9 +368,12 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
  * piece_cost + 1) and a_min * p_min is the lightest weight any of the
  * n_waves wavefronts has: every active wavefront gets at least m units.  A
  * wavefront takes the tiles whose first unit falls in its range.
+ * With window >= 1 a sequence of context L costs only the tiles from its
+ * window's first one, floor(max(L - window, 0) / 16), on.
  * decode_step uses n_first = the first workgroup on each compute unit (4
  * wavefronts per CU), weight_first = 100, weight_rest = young_weight_pct,
- * weight_odd = odd_weight_pct and weight_min_share = 256.  Writes up to
+ * weight_odd = odd_weight_pct, weight_min_share = 256 and the pool's
+ * window.  Writes up to
  * max_pieces rows of 6 int32 to pieces:
  * {wave, request, kv_head, first_tile, end_tile, flags} with flags bit 0 =
  * the piece is part of a split sequence, bit 1 = it is the wave's first
@@ -372,7 +385,8 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch,
                          int32_t n_kv_heads, int32_t max_tokens, int32_t n_waves,
                          int32_t min_units, int32_t piece_cost, int32_t n_first,
                          int32_t weight_first, int32_t weight_rest, int32_t weight_odd,
-                         int32_t weight_min_share, int32_t max_pieces, int32_t* pieces, int32_t* n_pieces,
+                         int32_t weight_min_share, int32_t window, int32_t max_pieces,
+                         int32_t* pieces, int32_t* n_pieces,
                          int32_t* splits);
 
 /* Tokens per tile, the kernel's unit of work (16). */

@@ -128,8 +128,14 @@ def decode_step(*, k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
                 block_tables: np.ndarray, context_lens: np.ndarray,
                 block_size: int, rope_theta: float,
                 k_scale: Optional[np.ndarray] = None,
-                v_scale: Optional[np.ndarray] = None) -> dict:
+                v_scale: Optional[np.ndarray] = None, window: int = 0) -> dict:
     """One decode step for a ragged batch, entirely on the CPU.
+
+    ``window`` >= 1 is sliding-window attention, which the "TensorRT-LLM"
+    glossary entry (inferensys.com) names among the patterns its kernels
+    exploit without defining it; the reading taken is the plainest one: the
+    new token attends to the last ``window`` tokens of the request, itself
+    included, i.e. tokens ``[max(0, L - window), L)``.  0 attends to all.
 
     Returns a dict with ``out`` (float64 ``[B, Hq, D]``), the updated pools
     ``k_pool``/``v_pool`` (copies; only slot ``L_b - 1`` of each request
@@ -168,8 +174,9 @@ def decode_step(*, k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
 
     for b in range(bsz):
         length = int(context_lens[b])
-        kc = gather_request(kp, block_tables[b], length, block_size)
-        vc = gather_request(vp, block_tables[b], length, block_size)
+        lo = max(0, length - window) if window > 0 else 0
+        kc = gather_request(kp, block_tables[b], length, block_size)[:, lo:]
+        vc = gather_request(vp, block_tables[b], length, block_size)[:, lo:]
         kf = kv_to_f64(kc, kv_dtype, k_scale)
         vf = kv_to_f64(vc, kv_dtype, v_scale)
         q_rot = rope_f64(io_to_f64(q[b], io_dtype), int(positions[b]),

@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
     "kv_pool_read_timing", "pkv_last_error",
     "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
-    "pkv_tile_tokens", "kv_pool_copy_blocks",
+    "pkv_tile_tokens", "kv_pool_copy_blocks", "kv_pool_set_window",
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
     "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
     "pkv_alloc_prepare_step",
@@ -63,7 +63,7 @@ class _Info(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("ring_tiles", ctypes.c_int32),
         ("min_units", ctypes.c_int32), ("piece_cost", ctypes.c_int32),
         ("young_weight_pct", ctypes.c_int32), ("n_first", ctypes.c_int32),
-        ("odd_weight_pct", ctypes.c_int32),
+        ("odd_weight_pct", ctypes.c_int32), ("window", ctypes.c_int32),
     ]
 
 
@@ -97,9 +97,10 @@ def load_library(path: str = LIB_PATH):
         "pkv_check_decode_args": (I32, [I64, I32, I32, I32, I32, I32, P, P, P, P, P,
                                         I32, P, I32, I32, P]),
         "pkv_rope_table_host": (I32, [D, I32, I32, FP, FP]),
-        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
+        "pkv_plan_host": (I32, [IP, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, IP, IP, IP]),
         "pkv_tile_tokens": (I32, []),
         "kv_pool_copy_blocks": (I32, [P, P, I32, P]),
+        "kv_pool_set_window": (I32, [P, I32]),
         "pkv_alloc_create": (I32, [I64, I32, I32, ctypes.POINTER(P)]),
         "pkv_alloc_destroy": (I32, [P]),
         "pkv_alloc_stats": (I32, [P, ctypes.POINTER(I64), IP]),
@@ -173,6 +174,10 @@ class KVPool:
         _check(_lib.kv_pool_set_tuning(self.handle, int(waves_per_cu), int(min_units),
                                        int(piece_cost), int(young_weight_pct),
                                        int(odd_weight_pct)))
+
+    def set_window(self, window: int) -> None:
+        """Attend to the last ``window`` tokens of each request (0 = all)."""
+        _check(_lib.kv_pool_set_window(self.handle, int(window)))
 
     def copy_blocks(self, pairs, stream=None) -> None:
         """Copy whole blocks, ``pairs`` an int32 ``[n, 2]`` device tensor of
@@ -416,7 +421,7 @@ def rope_table_host(theta: float, head_dim: int, max_position: int):
 def plan_host(context_lens, n_kv_heads: int, max_tokens: int, n_waves: int,
               min_units: int, piece_cost: int = 0, n_first: int = 0, weight_first: int = 1,
               weight_rest: int = 1, weight_min_share: int = 0, max_pieces: int = 1 << 20,
-              weight_odd: int = 100):
+              weight_odd: int = 100, window: int = 0):
     """Host replay of the kernel's work partition (numpy arrays): pieces
     ``[n, 6]`` and the per-wave split-sequence rows ``[n_waves, 4]``.  The
     first ``n_first`` wavefronts weigh ``weight_first``, the rest
@@ -434,7 +439,7 @@ def plan_host(context_lens, n_kv_heads: int, max_tokens: int, n_waves: int,
     _check(lib.pkv_plan_host(lens.ctypes.data_as(ip), int(lens.shape[0]), int(n_kv_heads),
                              int(max_tokens), int(n_waves), int(min_units), int(piece_cost),
                              int(n_first), int(weight_first), int(weight_rest), int(weight_odd),
-                             int(weight_min_share), int(max_pieces),
+                             int(weight_min_share), int(window), int(max_pieces),
                              pieces.ctypes.data_as(ip), ctypes.byref(n),
                              splits.ctypes.data_as(ip)))
     return pieces[:min(n.value, max_pieces)], splits

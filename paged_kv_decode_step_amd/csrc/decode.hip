@@ -309,16 +309,24 @@ template <int KCH> struct QOp<KV_FP8, KCH>  { f16x8_t v[KCH][2]; };
 template <int KCH> struct QOp<KV_F32, KCH>  { float v[KCH][4]; };
 
 // Position in the concatenation of the wave's sequences (wave-uniform).
+// Tiles are counted from the first one the sequence reads (lo, the first
+// tile of its attention window, 0 without one): tile j of the walk is tile
+// lo + j of the request's context.
 struct Walk {
   int b, h, j, n;   // request, KV head, tile in the sequence, tiles of the sequence
+  int lo;           // first tile of the request's context that is read
 };
 
-__device__ __forceinline__ void walk_next(Walk& w, const int* sP, int B, int hkv, int cost) {
+__device__ __forceinline__ void walk_next(Walk& w, const int* sP, const int* sLo, int B, int hkv,
+                                          int cost) {
   if (++w.j == w.n) {
     w.j = 0;
     if (++w.h == hkv) {
       w.h = 0;
-      if (++w.b < B) w.n = uniform(tiles_per_seq(sP, w.b, hkv, cost));
+      if (++w.b < B) {
+        w.n = uniform(tiles_per_seq(sP, w.b, hkv, cost));
+        w.lo = uniform(sLo[w.b]);
+      }
     }
   }
 }
@@ -334,6 +342,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   constexpr int R = C::RING;
   constexpr int PF = partial_floats(D);
   __shared__ int sP[kMaxBatch + 1];
+  __shared__ int sLo[kMaxBatch];       // first tile each request reads (its window's)
   __shared__ int sWsum[kBlockThreads / 64];
   __shared__ u32x4_t sKrow[kBlockThreads / 64][C::KROWS];   // appended key row
   __shared__ uint32_t sVrow[kBlockThreads / 64][D];          // appended value codes
@@ -358,7 +367,12 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int cost = p.piece_cost;
   // ---- work units per request (hkv sequences of tiles + cost each),
   // prefix-summed into LDS (every workgroup)
-  for (int i = tid; i < B; i += kBlockThreads) sP[i] = hkv * (tiles_of(lens[i], cap) + cost);
+  for (int i = tid; i < B; i += kBlockThreads) {
+    const int Li = lens[i];
+    const int lo = window_first_tile(Li, cap, p.window);
+    sLo[i] = lo;
+    sP[i] = hkv * (tiles_of(Li, cap) - lo + cost);
+  }
   __syncthreads();
   {
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
@@ -387,10 +401,12 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     __syncthreads();
   }
 
-  const int64_t U = sP[B];                               // work units
+  // work units (< 2^31, checked on the host); U and W live in scalar
+  // registers through the tile loop
+  const int64_t U = uniform(sP[B]);
   const WaveWeights ww = weights_for(U, p.n_waves, p.weight_min_share,
                                      WaveWeights{p.weight_first, p.weight_rest, p.n_first, p.weight_odd});
-  const int64_t W = active_waves(U, p.n_waves, p.min_units, ww);
+  const int64_t W = uniform((int)active_waves(U, p.n_waves, p.min_units, ww));
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
   if (wave >= W) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
@@ -421,6 +437,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
         w0.n = uniform(tiles_per_seq(sP, w0.b, hkv, cost));
       }
     }
+    w0.lo = w0.b < B ? uniform(sLo[w0.b]) : 0;
   }
   if (T <= 0) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
@@ -436,7 +453,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   Walk pw = w0;
   int p_left = T;
   auto load_blk = [&](const Walk& w) __attribute__((always_inline)) -> int {
-    return tables[(int64_t)w.b * p.max_blocks + (w.j >> C::LOG2TPB)];
+    return tables[(int64_t)w.b * p.max_blocks + ((w.j + w.lo) >> C::LOG2TPB)];
   };
   int pf_blk = load_blk(pw);
   int64_t pf_off = 0;
@@ -449,7 +466,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       bad_block |= pf_live ? 1u : 0u;
       blk = 0;
     }
-    pf_off = (((int64_t)blk * hkv + pw.h) * C::TPB + (pw.j & (C::TPB - 1))) * C::TILE_BYTES;
+    pf_off = (((int64_t)blk * hkv + pw.h) * C::TPB + ((pw.j + pw.lo) & (C::TPB - 1))) * C::TILE_BYTES;
     const char* base = pf_live ? kpool + pf_off : dummy;
 #pragma unroll
     for (int c = 0; c < C::KCH; ++c)
@@ -463,7 +480,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     if (pf_live) {
       --p_left;
       if (p_left > 0) {
-        walk_next(pw, sP, B, hkv, cost);
+        walk_next(pw, sP, sLo, B, hkv, cost);
         pf_blk = load_blk(pw);
       }
     }
@@ -481,12 +498,15 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   float m_run = -INFINITY, l_run = 0.f;
   float sscale = p.sm_scale_log2, vsc = 1.0f;
   int L = 1, pend = 1, slot = 0;
+  int lo_tok = 0;      // first token of the attention window
   bool split = false, app = false;
   int r0 = 0;
   uint32_t bad_len = 0, bad_pos = 0;
   int j0 = 0;
   // the split sequence whose first piece this wavefront holds (its last piece)
-  int4 split_hdr = make_int4(0, 0, 0, 0);
+  // (request, KV head, tiles, partial slot): its piece count is worked out
+  // after the tile loop, where its divisions cost no registers
+  int4 split_seq = make_int4(-1, 0, 0, 0);
 
   const int64_t out_row_stride = (int64_t)hkv * G;   // query heads per request
 
@@ -544,6 +564,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     bad_pos |= pos_ok ? 0u : 1u;
     posn = posn < 0 ? 0 : (posn >= p.max_pos ? p.max_pos - 1 : posn);
     L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
+    lo_tok = (p.window > 0 && L > p.window) ? L - p.window : 0;
     j0 = cw.j;
     pend = min(cw.n, j0 + (T - i));
     split = j0 > 0 || pend < cw.n;
@@ -780,17 +801,20 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   };
 
   // Online softmax over the tile (log2 domain) and P V.  On the sequence's
-  // last tile, tokens at or past L get score -inf (selected, never
-  // multiplied) and their values are zeroed, whatever the slots hold.
+  // last tile, tokens at or past L, and on the first tile of an attention
+  // window, tokens before it get score -inf (selected, never multiplied) and
+  // their values are zeroed, whatever the slots hold.
   auto softmax_pv = [&](f32x4_t a, TileRegs<C::KCH>& t, bool last) __attribute__((always_inline)) {
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = a[r] * sscale;
-    if (last) {
-      const int nv = L - (16 * cw.j + 4 * lq);   // valid tokens among this lane's four
+    if (last || (cw.j == 0 && lo_tok > 16 * cw.lo)) {
+      const int t0 = 16 * (cw.j + cw.lo) + 4 * lq;   // token of this lane's first score
+      const int nv = L - t0;                         // its tokens r < nv are in the context
+      const int nlo = lo_tok - t0;                   // and those r >= nlo in the window
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (r >= nv) s[r] = -INFINITY;
+        if (r >= nv || r < nlo) s[r] = -INFINITY;
       u32x4_t keep;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -798,7 +822,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 #pragma unroll
         for (int by = 0; by < 4; ++by) {
           const int e = ((4 * q + by) % (4 * C::ELEM)) / C::ELEM;   // token of byte
-          m |= (e < nv) ? (0xffu << (8 * by)) : 0u;
+          m |= (e < nv && e >= nlo) ? (0xffu << (8 * by)) : 0u;
         }
         keep[q] = m;
       }
@@ -917,11 +941,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       }
       wait_vector_memory();
     }
-    if (j0 == 0) {
-      const int64_t last = first_unit(sP, cw.b, cw.h, cw.n - 1, cw.n, cost);
-      const int np = (int)(wave_of_unit(last, U, W, ww) - wave + 1);
-      split_hdr = make_int4(1, cw.b * hkv + cw.h, np, slot);
-    }
+    if (j0 == 0) split_seq = make_int4(cw.b, cw.h, cw.n, slot);
   };
 
   // ---- main loop: consume tile i from slot i % R, refill it with tile i + R.
@@ -946,7 +966,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       issue_v(ring[u]);
       if (live) {
         if (i == T - 1 || last) end_piece();
-        walk_next(cw, sP, B, hkv, cost);
+        walk_next(cw, sP, sLo, B, hkv, cost);
       }
     }, std::make_integer_sequence<int, R>{});
   }
@@ -985,6 +1005,13 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     }
   }
 
+  int4 split_hdr = make_int4(0, 0, 0, 0);
+  if (split_seq.x >= 0) {
+    const int sb = uniform(split_seq.x), sh = uniform(split_seq.y), sn = uniform(split_seq.z);
+    const int64_t last = first_unit(sP, sb, sh, sn - 1, sn, cost);
+    const int np = (int)(wave_of_unit(last, U, W, ww) - wave + 1);
+    split_hdr = make_int4(1, sb * hkv + sh, np, uniform(split_seq.w));
+  }
   if (lane == 0) p.headers[wave] = split_hdr;
 }
 

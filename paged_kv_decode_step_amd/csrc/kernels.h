@@ -49,6 +49,7 @@ struct DecodeParams {
   int32_t weight_odd;        // parity weight of odd workgroups, percent of even ones' (1..100)
   int32_t weight_min_share;  // units per wavefront below which the weights are even
   float sm_scale_log2;       // log2(e) / sqrt(D)
+  int32_t window;            // attention window in tokens (0 = the whole context)
 };
 
 // Floats of one partial softmax state: the accumulator of all 64 lanes

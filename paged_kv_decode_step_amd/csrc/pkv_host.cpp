@@ -116,6 +116,7 @@ struct pkv_pool {
   int ring_tiles = 0;
   int young_pct = 100;      // share weight of later workgroups, % of the first's
   int odd_pct = 100;        // share weight of odd workgroups, % of the even ones'
+  int window = 0;           // attention window in tokens (0 = the whole context)
   // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -329,6 +330,7 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->piece_cost = pool->piece_cost;
   info->young_weight_pct = pool->young_pct;
   info->odd_weight_pct = pool->odd_pct;
+  info->window = pool->window;
   info->n_first = std::min(pool->n_waves, 4 * pool->cus);
   return PKV_OK;
 }
@@ -506,6 +508,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.weight_odd = pool->odd_pct;
   p.weight_min_share = pkv::kWeightMinShare;
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
+  p.window = pool->window;
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
     const size_t need = 4 * (size_t)(pool->timed_calls + 1);
@@ -521,6 +524,13 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   hipError_t e = pkv::launch_decode(kv_kind(pool->kv_dtype), pool->head_dim, pool->block_size, p,
                                     st, ev);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return PKV_OK;
+}
+
+pkv_status kv_pool_set_window(pkv_pool* pool, int32_t window) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (window < 0) return fail(PKV_ERR_INVALID, "window must be >= 0 (0 = none)");
+  pool->window = window;
   return PKV_OK;
 }
 
@@ -581,7 +591,7 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
                          int32_t max_tokens, int32_t n_waves, int32_t min_units,
                          int32_t piece_cost, int32_t n_first, int32_t weight_first,
                          int32_t weight_rest, int32_t weight_odd, int32_t weight_min_share,
-                         int32_t max_pieces, int32_t* pieces,
+                         int32_t window, int32_t max_pieces, int32_t* pieces,
                          int32_t* n_pieces, int32_t* splits) {
   if (!context_lens || !n_pieces || !splits || (max_pieces > 0 && !pieces))
     return fail(PKV_ERR_INVALID, "null argument");
@@ -592,11 +602,13 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
   if (n_first < 0 || weight_rest < 1 || weight_first < weight_rest || weight_first > 1000)
     return fail(PKV_ERR_INVALID, "need n_first >= 0 and 1 <= weight_rest <= weight_first <= 1000");
   if (weight_odd < 1 || weight_odd > 100) return fail(PKV_ERR_INVALID, "weight_odd must be in [1, 100]");
+  if (window < 0) return fail(PKV_ERR_INVALID, "window must be >= 0");
   if (weight_min_share < 0) return fail(PKV_ERR_INVALID, "weight_min_share must be >= 0");
   const int hkv = n_kv_heads, cost = piece_cost;
   std::vector<int> P(batch + 1, 0);
   for (int b = 0; b < batch; ++b)
-    P[b + 1] = P[b] + hkv * (pkv::tiles_of(context_lens[b], max_tokens) + cost);
+    P[b + 1] = P[b] + hkv * (pkv::tiles_of(context_lens[b], max_tokens) -
+                              pkv::window_first_tile(context_lens[b], max_tokens, window) + cost);
   const int64_t C = P[batch];
   const pkv::WaveWeights ww = pkv::weights_for(
       C, n_waves, weight_min_share, pkv::WaveWeights{weight_first, weight_rest, n_first, weight_odd});

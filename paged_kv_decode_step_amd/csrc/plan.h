@@ -78,6 +78,17 @@ PKV_HD inline int tiles_of(int L, int cap) {
   return n < 1 ? 1 : n;
 }
 
+// First tile a sequence of context length L (clamped to [0, cap]) reads: with
+// an attention window of `window` >= 1 tokens the step attends to the tokens
+// [L - window, L), so the whole tiles before token L - window are skipped;
+// without one (window 0) it is tile 0.  A sequence then reads
+// tiles_of(L, cap) - window_first_tile(L, cap, window) >= 1 tiles.
+PKV_HD inline int window_first_tile(int L, int cap, int window) {
+  if (L < 0) L = 0;
+  if (L > cap) L = cap;
+  return (window > 0 && L > window) ? (L - window) >> 4 : 0;
+}
+
 // Weights of the wavefronts.  Wavefront w belongs to workgroup w / 4; its
 // weight is its age weight (wa for the first n_first wavefronts, the first
 // workgroup that lands on each compute unit, wb for the others, wa >= wb >= 1)
@@ -86,7 +97,7 @@ PKV_HD inline int tiles_of(int L, int cap) {
 // so odd workgroups run on odd XCDs, which were measured to stream about a
 // tenth slower than the even ones.
 struct WaveWeights {
-  int64_t wa, wb, n_first, po;
+  int32_t wa, wb, n_first, po;
 };
 
 // The weights in force for a step of n_units units: the given ones when

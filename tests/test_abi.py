@@ -101,7 +101,7 @@ def test_tile_tokens():
 
 # ---- work partition ---------------------------------------------------------
 def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=1, wr=1,
-                        min_share=0, wo=100):
+                        min_share=0, wo=100, window=0):
     """The partition written out plainly: sequences (b, h) in order, each cut
     into max(1, ceil(min(L, cap)/16)) tiles and costing its tiles plus
     `cost` units (tile 0 owns cost + 1 units); wave w weighs (wf if
@@ -109,8 +109,14 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
     whose exact share for a wave of the lightest of all n_waves weights is
     >= max(min_units, cost + 1) units are used (found by trying every
     count); the units are cut at floor(total * weights before w / all
-    weights) and each tile is owned by the wave holding its first unit."""
-    ns = [max(1, -(-min(max(int(L), 0), cap) // 16)) for L in lens]
+    weights) and each tile is owned by the wave holding its first unit.  With a
+    window of W >= 1 tokens a sequence's tiles start at the one holding token
+    L - W (when L > W), and are numbered from there."""
+    def tiles(L):
+        L = min(max(int(L), 0), cap)
+        lo = (L - window) // 16 if window > 0 and L > window else 0
+        return max(1, -(-L // 16)) - lo
+    ns = [tiles(L) for L in lens]
     seqs = [(b, h, ns[b]) for b in range(len(lens)) for h in range(hkv)]
     first_units = []
     u = 0
@@ -227,3 +233,21 @@ def test_piece_cost_gives_many_piece_waves_fewer_tiles():
     t0, t5 = tiles(p0), tiles(p5)
     assert t0.max() - t0.min() <= 1
     assert t5[3] < t0[3] and t5[0] > t0[0]
+
+
+@pytest.mark.parametrize("window", [1, 15, 16, 17, 40, 100, 5000])
+def test_partition_with_a_window_reads_only_the_window(window):
+    lens = [1, 16, 17, 40, 100, 300, 1000, 33, 5000]
+    cap = 1 << 20
+    for waves, cost in ((8, 0), (40, 3), (200, 6)):
+        pieces, splits = pkv.plan_host(lens, 2, cap, waves, 1, cost, window=window)
+        owner, bounds, we, seqs = reference_partition(lens, 2, cap, waves, 1, cost, window=window)
+        seen = {}
+        for w, b, h, t0, t1, fl in pieces:
+            for t in range(t0, t1):
+                seen[(b, h, t)] = w
+        assert seen == owner
+        for b, h, n in seqs:
+            L = lens[b]
+            lo = (L - window) // 16 if L > window else 0
+            assert n == -(-L // 16) - lo       # the tiles holding tokens [L - window, L)
