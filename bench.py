@@ -35,18 +35,24 @@ METRIC = "paged decode attention: HBM GB/s (% of peak) and decode tokens/s per l
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
-def algorithmic_bytes(wl) -> int:
+def algorithmic_bytes(wl, window: int = 0) -> int:
     """Bytes the step must move: cached K/V read once per KV head, the new
     K/V written, q/k_new/v_new read, out written, the block-table entries,
-    positions and lengths, the RoPE rows and (fp8) the scales."""
+    positions and lengths, the RoPE rows and (fp8) the scales.  With an
+    attention window of W tokens only the last W tokens of a request (the
+    new one included) and the table entries of their blocks count."""
     c = wl.cfg
     s_kv, s_io = ELEM[c.kv_dtype], ELEM[c.io_dtype]
     L = wl.context_lens.astype(np.int64)
+    bs = c.block_size
+    first = np.zeros_like(L)
+    if window > 0:
+        first = np.maximum(L - window, 0)
     per_tok = 2 * c.n_kv_heads * c.head_dim * s_kv
-    total = int(((L - 1) * per_tok).sum())                       # read cached K, V
+    total = int(((L - first - 1) * per_tok).sum())               # read cached K, V
     total += wl.batch * per_tok                                  # write new K, V
     total += wl.batch * (2 * c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * s_io
-    total += int((4 * ((L + c.block_size - 1) // c.block_size) + 8).sum())
+    total += int((4 * ((L + bs - 1) // bs - first // bs) + 8).sum())
     total += wl.batch * c.head_dim * 4                           # cos + sin rows
     if c.kv_dtype == "fp8":
         total += 16 * c.n_kv_heads
@@ -153,7 +159,7 @@ def setup_layers(wl, n_layers, device):
     return pools, tens, scales
 
 
-def cpu_baseline(wl, pool, tens, scales, budget_s: float):
+def cpu_baseline(wl, pool, tens, scales, budget_s: float, window: int = 0):
     """Time the CPU oracle on leading requests of the workload until about
     `budget_s` seconds of work, reading their inputs back from the device."""
     import torch
@@ -195,9 +201,9 @@ def cpu_baseline(wl, pool, tens, scales, budget_s: float):
                                v_new=arrs["v_new"], positions=mwl.positions,
                                block_tables=mwl.block_tables, context_lens=mwl.context_lens,
                                block_size=c.block_size, rope_theta=c.rope_theta,
-                               k_scale=arrs["k_scale"], v_scale=arrs["v_scale"])
+                               k_scale=arrs["k_scale"], v_scale=arrs["v_scale"], window=window)
             elapsed += time.perf_counter() - t0
-            done_bytes += algorithmic_bytes(mwl)
+            done_bytes += algorithmic_bytes(mwl, window)
             done_req += 1
             if elapsed >= budget_s:
                 budget_hit = True
@@ -218,6 +224,55 @@ def cpu_baseline(wl, pool, tens, scales, budget_s: float):
     }
 
 
+def allocator_bench(wl, device, steps: int) -> dict:
+    """Host cost of the allocator's step for the workload's batch (every
+    request grows by one token; half of them forked from a parent so their
+    half-full last blocks are copied on write), and the device copy of whole
+    blocks: bytes = 2 (K and V) x 2 (read and write) x block bytes per pair."""
+    import torch
+    import paged_kv_decode_step_amd as pkv
+
+    c = wl.cfg
+    lens = wl.context_lens.astype(np.int64)
+    nb = int(((lens + c.block_size) // c.block_size).sum()) * 2 + 16
+    alloc = pkv.BlockAllocator(nb, c.block_size, 2 * wl.batch + 1)
+    seqs = [alloc.add(int(L) - 1) for L in lens]
+    reps, t_host = max(1, min(steps, 50)), 0.0
+    maxb = int(wl.block_tables.shape[1]) + (reps + 2) // c.block_size + 2
+    alloc.prepare_step(seqs, maxb)          # first touch of the host arrays
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        alloc.prepare_step(seqs, maxb)
+        t_host += time.perf_counter() - t0
+    # copy on write: fork every other request, then one step copies each
+    # shared half-full block once
+    kids = [alloc.fork(s) for s in seqs[::2]]
+    _, _, _, copies = alloc.prepare_step(seqs[::2], maxb)
+    alloc.close()
+    pool = pkv.KVPool(nb, c.block_size, c.n_kv_heads, c.head_dim, c.kv_dtype)
+    pairs = torch.from_numpy(np.ascontiguousarray(copies)).to(device)
+    block_bytes = c.n_kv_heads * c.block_size * c.head_dim * ELEM[c.kv_dtype]
+    for _ in range(3):
+        pool.copy_blocks(pairs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_rep = max(10, steps)
+    e0.record()
+    for _ in range(n_rep):
+        pool.copy_blocks(pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_rep
+    pool.close()
+    moved = 4 * block_bytes * int(pairs.shape[0])
+    return {"metric": "block allocator: host prepare_step us per decode step; device block "
+                      "copy GB/s", "workload": c.name, "batch": wl.batch,
+            "prepare_step_us": round(1e6 * t_host / reps, 2),
+            "forked": len(kids), "copies": int(pairs.shape[0]),
+            "copy_ms": round(ms, 5), "copy_GBps": round(moved / (ms * 1e-3) / 1e9, 2),
+            "block_bytes": block_bytes}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +282,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window attention over the last W tokens (0 = whole context)")
+    ap.add_argument("--allocator", action="store_true",
+                    help="only measure the block allocator's host step (prepare_step for the "
+                         "workload's batch) and the device block copy, one JSON line")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the multi-layer step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -254,11 +314,16 @@ def main():
         return
     wl = workloads.make_workload(args.config)
     c = wl.cfg
-    alg = algorithmic_bytes(wl)
+    if args.allocator:
+        print(json.dumps(allocator_bench(wl, device, args.steps)), flush=True)
+        return
+    alg = algorithmic_bytes(wl, args.window)
     kv_bytes = int(((wl.context_lens.astype(np.int64)) * 2 * c.n_kv_heads * c.head_dim
                     * ELEM[c.kv_dtype]).sum())
-    n_layers = max(1, math.ceil(args.min_cold_bytes / kv_bytes))
+    n_layers = max(1, math.ceil(args.min_cold_bytes / (min(kv_bytes, alg) if args.window else kv_bytes)))
     pools, t, scales = setup_layers(wl, n_layers, device)
+    for p in pools:
+        p.set_window(args.window)
     print(f"# workload {c.name}: {wl.batch} requests, {alg/1e9:.3f} GB algorithmic per step, "
           f"{n_layers} pool copies, {pools[0].info()['n_waves']} wavefronts", file=sys.stderr,
           flush=True)
@@ -347,7 +412,7 @@ def main():
                    "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
                    "block_size": c.block_size, "kv_dtype": c.kv_dtype,
                    "io_dtype": c.io_dtype, "mean_context": float(wl.context_lens.mean()),
-                   "pool_copies": n_layers},
+                   "pool_copies": n_layers, "window": args.window},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s_per_layer": round(wl.batch / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,
@@ -364,7 +429,8 @@ def main():
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(wl, pools[0], t, scales, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, pools[0], t, scales, args.cpu_budget,
+                                              args.window)
     for p in pools:
         p.close()
     print(json.dumps(result), flush=True)
