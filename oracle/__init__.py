@@ -41,7 +41,7 @@ pool.  No function here is "parity unpinned".
 from .codecs import (bf16_bits_from_f32, bf16_bits_to_f32, bf16_bits_to_f64,
                      fp8_code_value, fp8_encode, fp8_decode, FP8_MAX)
 from .rope import inv_freq, rope_rows_f32, rope_f64, rope_k_f32
-from .decode import (decode_step, gather_request, attention_request,
+from .decode import (decode_step, decode_step_multi, gather_request, attention_request,
                      io_to_f64, io_to_f32, kv_to_f64, fp8_inverse_scale,
                      cast_to_kv)
 from .variants import (padded_static_batch, split_merge,
@@ -53,7 +53,7 @@ __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f32", "bf16_bits_to_f64",
     "fp8_code_value", "fp8_encode", "fp8_decode", "FP8_MAX",
     "inv_freq", "rope_rows_f32", "rope_f64", "rope_k_f32",
-    "decode_step", "gather_request", "attention_request", "io_to_f64",
+    "decode_step", "decode_step_multi", "gather_request", "attention_request", "io_to_f64",
     "io_to_f32", "kv_to_f64", "fp8_inverse_scale", "cast_to_kv",
     "padded_static_batch", "split_merge", "brute_force_rotate_key",
     "brute_force_attention", "BlockAllocator", "AllocError", "DenseHistories",

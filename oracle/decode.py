@@ -184,3 +184,56 @@ def decode_step(*, k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
         out[b] = attention_request(q_rot, kf, vf)
     return {"out": out, "k_pool": kp, "v_pool": vp, "k_app": k_app,
             "v_app": v_app}
+
+
+def decode_step_multi(*, k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
+                      io_dtype: str, q: np.ndarray, k_new: np.ndarray,
+                      v_new: np.ndarray, positions: np.ndarray,
+                      block_tables: np.ndarray, context_lens: np.ndarray,
+                      block_size: int, rope_theta: float,
+                      k_scale: Optional[np.ndarray] = None,
+                      v_scale: Optional[np.ndarray] = None) -> dict:
+    """A step that brings T new tokens per request (speculative verification of
+    draft tokens, or the tail of a chunked prefill; the pages name both
+    without writing the attention out).  Reading taken: ``q [B, T, Hq, D]``,
+    ``k_new``/``v_new [B, T, Hkv, D]``; ``context_lens`` counts all T new
+    tokens, new token i goes to slot ``L - T + i`` at RoPE position
+    ``positions[b] + i``, and its query attends causally to the tokens
+    ``[0, L - T + i]``, i.e. to the cache and to the new tokens up to itself.
+    All T appends happen before any attention.  Returns ``out [B, T, Hq, D]``
+    (float64) and the updated pools.
+    """
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    bsz, tq = q.shape[0], q.shape[1]
+    hkv, d = kp.shape[1], kp.shape[3]
+    hq = q.shape[2]
+    if kv_dtype == "fp8":
+        inv_k = fp8_inverse_scale(k_scale)
+        inv_v = fp8_inverse_scale(v_scale)
+    else:
+        inv_k = inv_v = [None] * hkv
+    out = np.empty((bsz, tq, hq, d), dtype=np.float64)
+    for b in range(bsz):
+        length = int(context_lens[b])
+        for i in range(tq):
+            slot = length - tq + i
+            pos = int(positions[b]) + i
+            phys = int(block_tables[b, slot // block_size])
+            off = slot % block_size
+            c_row, s_row = rope_rows_f32(rope_theta, d, [pos])
+            k32 = io_to_f32(k_new[b, i], io_dtype)
+            v32 = io_to_f32(v_new[b, i], io_dtype)
+            for h in range(hkv):
+                kp[phys, h, off, :] = cast_to_kv(rope_k_f32(k32[h], c_row[0], s_row[0]),
+                                                 kv_dtype, inv_k[h])
+                vp[phys, h, off, :] = cast_to_kv(v32[h], kv_dtype, inv_v[h])
+    for b in range(bsz):
+        length = int(context_lens[b])
+        kf = kv_to_f64(gather_request(kp, block_tables[b], length, block_size), kv_dtype, k_scale)
+        vf = kv_to_f64(gather_request(vp, block_tables[b], length, block_size), kv_dtype, v_scale)
+        for i in range(tq):
+            seen = length - tq + i + 1
+            q_rot = rope_f64(io_to_f64(q[b, i], io_dtype), int(positions[b]) + i, rope_theta)
+            out[b, i] = attention_request(q_rot, kf[:, :seen], vf[:, :seen])
+    return {"out": out, "k_pool": kp, "v_pool": vp}
