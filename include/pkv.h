@@ -187,6 +187,29 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
                        int32_t batch, int32_t n_q_heads, void* out,
                        void* stream);
 
+/* A step that brings n_new >= 1 new tokens per request: a chunk of a long
+ * prompt processed beside decoding requests ("Lesson 13.17 TensorRT-LLM:
+ * NVIDIA's Optimized Inference Engine", section "The paged KV cache, in-flight
+ * batching and CUDA graphs"), or draft tokens verified in one pass (same page,
+ * section "Speculative decoding and running one model across many GPUs";
+ * "Scaling TensorRT-LLM: Kernel Fusion and Inflight Batching in Production",
+ * section "3. Speculative Decoding for Tail Latency").  Layouts as
+ * decode_step with a token axis: q and out [B][n_new][n_q_heads][head_dim],
+ * k_new and v_new [B][n_new][n_kv_heads][head_dim]; positions[b] is the RoPE
+ * position of the first new token (new token i is at positions[b] + i);
+ * context_lens[b] counts all n_new new tokens, which go to slots
+ * L - n_new .. L - 1.  Query i attends to the tokens [0, L - n_new + i]
+ * (causal inside the new tokens).  n_new = 1 is decode_step.  For n_new > 1:
+ * a bf16 or fp8 cache, no attention window, (n_q_heads / n_kv_heads) x n_new
+ * <= 16 (PKV_ERR_UNSUPPORTED otherwise), a RoPE table of >= n_new positions;
+ * the new tokens are appended by a separate launch before the attention
+ * kernel.  The blocks holding the new tokens must be the request's own. */
+pkv_status decode_step_multi(pkv_pool* pool, const void* q, const void* k_new,
+                             const void* v_new, pkv_dtype io_dtype, int32_t n_new,
+                             const int32_t* positions, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t batch, int32_t n_q_heads, void* out, void* stream);
+
 /* Read and clear the device-side range flags raised by earlier decode_step
  * calls (synchronises the device).  Bit 0: a block id outside
  * [0, num_blocks); bit 1: a position outside [0, max_position); bit 2: a

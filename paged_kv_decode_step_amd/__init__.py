@@ -19,7 +19,7 @@ import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
 __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
-    "EXPORTED_SYMBOLS", "BlockAllocator",
+    "EXPORTED_SYMBOLS", "BlockAllocator", "decode_step_multi",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
     "kv_pool_read_timing", "pkv_last_error",
     "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
-    "pkv_tile_tokens", "kv_pool_copy_blocks", "kv_pool_set_window",
+    "pkv_tile_tokens", "kv_pool_copy_blocks", "kv_pool_set_window", "decode_step_multi",
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
     "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
     "pkv_alloc_prepare_step",
@@ -101,6 +101,7 @@ def load_library(path: str = LIB_PATH):
         "pkv_tile_tokens": (I32, []),
         "kv_pool_copy_blocks": (I32, [P, P, I32, P]),
         "kv_pool_set_window": (I32, [P, I32]),
+        "decode_step_multi": (I32, [P, P, P, P, I32, I32, P, P, I32, P, I32, I32, P, P]),
         "pkv_alloc_create": (I32, [I64, I32, I32, ctypes.POINTER(P)]),
         "pkv_alloc_destroy": (I32, [P]),
         "pkv_alloc_stats": (I32, [P, ctypes.POINTER(I64), IP]),
@@ -378,6 +379,47 @@ class BlockAllocator:
                                            lens.ctypes.data_as(ip), pos.ctypes.data_as(ip),
                                            copies.ctypes.data_as(ip), mc, ctypes.byref(n)))
         return tables[:b], lens[:b], pos[:b], copies[:n.value]
+
+
+def decode_step_multi(pool: KVPool, q, k_new, v_new, positions, block_tables,
+                      context_lens, out, stream=None) -> None:
+    """Launch a step with T new tokens per request (``decode_step_multi``):
+    ``q``/``out`` ``[B, T, Hq, D]``, ``k_new``/``v_new`` ``[B, T, Hkv, D]``,
+    ``positions`` the first new token's position, ``context_lens`` counting
+    all T new tokens; query i attends to the tokens ``[0, L - T + i]``."""
+    lib = load_library()
+    io = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if io is None:
+        raise PkvError(-1, f"unsupported io dtype {q.dtype}")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("out", out),
+                    ("positions", positions), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise PkvError(-1, f"{name} must be contiguous on the GPU")
+    for name, t in (("positions", positions), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        if t.dtype != torch.int32:
+            raise PkvError(-1, f"{name} must be int32")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("out", out)):
+        if t.dtype != q.dtype:
+            raise PkvError(-1, f"{name} must have q's dtype")
+    if q.dim() != 4 or q.shape[3] != pool.head_dim or out.shape != q.shape:
+        raise PkvError(-1, "q/out must be [B, T, Hq, head_dim]")
+    batch, tq, hq = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    if tuple(k_new.shape) != (batch, tq, pool.n_kv_heads, pool.head_dim) or k_new.shape != v_new.shape:
+        raise PkvError(-1, "k_new/v_new must be [B, T, Hkv, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise PkvError(-1, "block_tables must be [B, max_blocks]")
+    if positions.numel() != batch or context_lens.numel() != batch:
+        raise PkvError(-1, "positions/context_lens must be [B]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.decode_step_multi(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), DTYPES[io], tq,
+                                 _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
+                                 _ptr(context_lens), batch, hq, _ptr(out),
+                                 ctypes.c_void_p(stream)))
 
 
 # ---- host-only helpers -----------------------------------------------------

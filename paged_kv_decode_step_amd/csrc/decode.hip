@@ -332,7 +332,10 @@ __device__ __forceinline__ void walk_next(Walk& w, const int* sP, const int* sLo
 }
 
 // ---------------------------------------------------------------- kernel
-template <int KV, int D, int BS>
+// MQ: every request brings n_qtok > 1 new tokens (appended beforehand by
+// decode_append_kernel); MFMA column lr = qi * G + g holds query head g of new
+// token qi, which attends causally to the tokens [0, L - n_qtok + qi].
+template <int KV, int D, int BS, bool MQ>
 __global__ __launch_bounds__(kBlockThreads)
 __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU, PKV_WAVES_PER_EU)))
 void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
@@ -362,6 +365,9 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int wid = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int B = p.batch, hkv = p.n_kv_heads, G = p.group;
+  const int TQ = MQ ? p.n_qtok : 1;           // new tokens per request
+  const int NC = G * TQ;                      // MFMA columns in use (<= 16)
+  const int lane_qi = MQ ? (lr < NC ? lr : 0) / G : 0;   // new token of this lane's column
   const int cap = p.max_blocks * BS;
 
   const int cost = p.piece_cost;
@@ -521,7 +527,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   // Room for an item of `words` payload words: the word index of its
   // header, or -1 (the write is then made at once).
   auto q_reserve = [&](int words) __attribute__((always_inline)) -> int {
-    if (q_used + 1 + words > QW) return -1;
+    if (MQ || q_used + 1 + words > QW) return -1;
     const int at = q_used;
     q_used += 1 + words;
     return at;
@@ -559,25 +565,27 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     const int Lraw = lens[b];
     int posn = poss[b];
     const bool len_ok = Lraw >= 1 && Lraw <= cap;
-    const bool pos_ok = posn >= 0 && posn < p.max_pos;
+    const bool pos_ok = posn >= 0 && posn + TQ - 1 < p.max_pos;
     bad_len |= len_ok ? 0u : 1u;
     bad_pos |= pos_ok ? 0u : 1u;
-    posn = posn < 0 ? 0 : (posn >= p.max_pos ? p.max_pos - 1 : posn);
+    posn = posn < 0 ? 0 : (posn + TQ - 1 >= p.max_pos ? p.max_pos - TQ : posn);
     L = Lraw < 0 ? 0 : (Lraw > cap ? cap : Lraw);
     lo_tok = (p.window > 0 && L > p.window) ? L - p.window : 0;
     j0 = cw.j;
     pend = min(cw.n, j0 + (T - i));
     split = j0 > 0 || pend < cw.n;
     slot = i == 0 ? 0 : 1;
-    app = len_ok && pend == cw.n;
+    app = !MQ && len_ok && pend == cw.n;
 
-    // Rotated query of head lr at this lane's dims (fp32 RoPE from the
-    // table).  Heads past G load head 0 of the group and are zeroed.
-    const int hq = h * G + (lr < G ? lr : 0);
-    const bool hvalid = lr < G;
-    const int64_t qrow = ((int64_t)b * out_row_stride + hq) * D;
-    const float* crow = p.rope_cos + (int64_t)posn * C::HALF;
-    const float* srow = p.rope_sin + (int64_t)posn * C::HALF;
+    // Rotated query of column lr at this lane's dims (fp32 RoPE from the
+    // table): head g of new token qi (lr = qi * G + g) at position posn + qi.
+    // Columns past the last load column 0 and are zeroed.
+    const int col = lr < NC ? lr : 0;
+    const int hq = h * G + (col - lane_qi * G);
+    const bool hvalid = lr < NC;
+    const int64_t qrow = (((int64_t)b * TQ + lane_qi) * out_row_stride + hq) * D;
+    const float* crow = p.rope_cos + (int64_t)(posn + lane_qi) * C::HALF;
+    const float* srow = p.rope_sin + (int64_t)(posn + lane_qi) * C::HALF;
     // Chunks c and c + KCH/2 hold the two halves of the rotate-half pairs
     // (dims d and d + D/2) and share one row of the cos/sin table; with a
     // single chunk, lanes lq < 2 hold the lower half and lq >= 2 the upper.
@@ -808,13 +816,16 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = a[r] * sscale;
-    if (last || (cw.j == 0 && lo_tok > 16 * cw.lo)) {
+    if (last || (cw.j == 0 && lo_tok > 16 * cw.lo) ||
+        (MQ && 16 * (cw.j + cw.lo + 1) > L - TQ)) {
       const int t0 = 16 * (cw.j + cw.lo) + 4 * lq;   // token of this lane's first score
       const int nv = L - t0;                         // its tokens r < nv are in the context
       const int nlo = lo_tok - t0;                   // and those r >= nlo in the window
+      // and those r < nc are visible to the column's new token (causal)
+      const int nc = MQ ? L - TQ + lane_qi + 1 - t0 : nv;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (r >= nv || r < nlo) s[r] = -INFINITY;
+        if (r >= nc || r < nlo) s[r] = -INFINITY;
       u32x4_t keep;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -887,8 +898,8 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   auto store_out = [&](int b, int h, const f32x4_t (&o)[C::NT], float scale) __attribute__((always_inline)) {
     const int at = q_reserve(out_words);
     if (at >= 0) q_header(at, Q_OUT, out_words, b * hkv + h, 0, 0);
-    if (lr >= G) return;
-    const int64_t row = ((int64_t)b * out_row_stride + h * G + lr) * D;
+    if (lr >= NC) return;
+    const int64_t row = (((int64_t)b * TQ + lane_qi) * out_row_stride + h * G + (lr - lane_qi * G)) * D;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const int d = 16 * nt + 4 * lq;
@@ -930,7 +941,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       }
     } else {
       float* part = p.partials + ((int64_t)wave * 2 + slot) * PF;
-      if (lr < G) {
+      if (lr < NC) {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
           *reinterpret_cast<f32x4_t*>(part + lr * D + 16 * nt + 4 * lq) = acc[nt] * vsc;
@@ -1030,10 +1041,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
   const int w = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
   const int4 hdr = p.headers[w];
   if (!uniform(hdr.x)) return;
-  const int G = p.group, hkv = p.n_kv_heads;
+  const int G = p.group, hkv = p.n_kv_heads, TQ = p.n_qtok;
   const int seq = uniform(hdr.y), np = uniform(hdr.z), slot0 = uniform(hdr.w);
   const int b = seq / hkv, h = seq - (seq / hkv) * hkv;
-  const int nchunk = G * D / 4;
+  const int nchunk = G * TQ * D / 4;          // columns (query head g of new token qi) x D
   int ch[KC], hd[KC];
   bool ok[KC];
   float M[KC], den[KC];
@@ -1086,7 +1097,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
     if (!ok[k]) continue;
     const float inv = den[k] > 0.f ? 1.0f / den[k] : 0.f;
     const int d = 4 * ch[k] - hd[k] * D;
-    const int64_t row = ((int64_t)b * hkv * G + h * G + hd[k]) * D;
+    const int qi = TQ > 1 ? hd[k] / G : 0;     // new token of the column
+    const int64_t row = (((int64_t)b * TQ + qi) * hkv * G + h * G + (hd[k] - qi * G)) * D;
     if constexpr (IO_BF16) {
       u32x2_t o;
       o[0] = bf16_rne(num[k][0] * inv) | (bf16_rne(num[k][1] * inv) << 16);
@@ -1102,7 +1114,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
 // two >= G*D / 256.
 template <bool IO_BF16, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
-  const int need = (p.group * D / 4 + 63) / 64;
+  const int need = (p.group * p.n_qtok * D / 4 + 63) / 64;
   const dim3 grid(p.n_waves / 4), block(kBlockThreads);
   hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
   if (need <= 1) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 1>), grid, block, 0, stream, e0, e1, 0, p);
@@ -1112,14 +1124,115 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
   return hipGetLastError();
 }
 
+// The append of a step with n_qtok > 1 new tokens per request: one wavefront
+// per (request, new token i, KV head) writes the rotated key and the value of
+// token i to slot L - n_qtok + i, with the same arithmetic as the fused
+// append (RoPE at position positions[b] + i in separate fp32 multiplies and
+// adds, then the cast to the cache type).  It runs before the attention
+// kernel, so every new token is in the pool when the queries read it.
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(kBlockThreads) void decode_append_kernel(DecodeParams p) {
+  using C = Cfg<KV, D, BS>;
+  const int lane = threadIdx.x & 63;
+  const int hkv = p.n_kv_heads, TQ = p.n_qtok;
+  const int64_t item = (int64_t)blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6);
+  if (item >= (int64_t)p.batch * TQ * hkv) return;
+  const int h = (int)(item % hkv);
+  const int64_t bi = item / hkv;
+  const int i = (int)(bi % TQ), b = (int)(bi / TQ);
+  const int cap = p.max_blocks * BS;
+  const int L = p.context_lens[b];
+  const int pos0 = p.positions[b];
+  if (L < TQ || L > cap) {
+    if (lane == 0) p.err[2] = 1u;
+    return;
+  }
+  if (pos0 < 0 || pos0 + TQ - 1 >= p.max_pos) {
+    if (lane == 0) p.err[1] = 1u;
+    return;
+  }
+  const int slot = L - TQ + i;
+  const int blk = p.block_tables[(int64_t)b * p.max_blocks + slot / BS];
+  if ((unsigned)blk >= (unsigned)p.num_blocks) {
+    if (lane == 0) p.err[0] = 1u;
+    return;
+  }
+  const float* crow = p.rope_cos + (int64_t)(pos0 + i) * C::HALF;
+  const float* srow = p.rope_sin + (int64_t)(pos0 + i) * C::HALF;
+  const int64_t nrow = (((int64_t)b * TQ + i) * hkv + h) * D;
+  float inv_k = 1.0f, inv_v = 1.0f;
+  if constexpr (KV == KV_FP8) {
+    inv_k = p.fp8_scales[2 * hkv + h];
+    inv_v = p.fp8_scales[3 * hkv + h];
+  }
+  const int r = slot & (BS - 1);
+  const int64_t toff = (((int64_t)blk * hkv + h) * C::TPB + ((r / kTileTokens) & (C::TPB - 1))) *
+                       C::TILE_BYTES;
+  const int r16 = r & 15;
+  char* kpool = static_cast<char*>(p.k_pool);
+  char* vpool = static_cast<char*>(p.v_pool);
+  if (lane < C::KROWS) {
+    const int d0 = C::X * lane;
+    const bool lo = d0 < C::HALF;
+    const int pd0 = lo ? d0 + C::HALF : d0 - C::HALF;
+    const int i0 = lo ? d0 : pd0;
+    float x[C::X], xp[C::X], cs[C::X], sn[C::X];
+    load_row_f32<C::IO_BF16, C::X>(p.k_new, nrow + d0, x);
+    load_row_f32<C::IO_BF16, C::X>(p.k_new, nrow + pd0, xp);
+    load_f32<C::X>(crow + i0, cs);
+    load_f32<C::X>(srow + i0, sn);
+    uint32_t enc[C::X];
+#pragma unroll
+    for (int e = 0; e < C::X; ++e) {
+      const float a = x[e] * cs[e];
+      const float bb = xp[e] * sn[e];
+      enc[e] = encode_kv<KV>(lo ? a - bb : a + bb, inv_k);
+    }
+    u32x4_t row;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 4 / C::ELEM; ++k) w |= enc[i2 * (4 / C::ELEM) + k] << (k * C::ELEM * 8);
+      row[i2] = w;
+    }
+    *reinterpret_cast<u32x4_t*>(kpool + toff + (lane * 16 + r16) * 16) = row;
+  }
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    const int d = lane + 64 * k;
+    const uint32_t code = encode_kv<KV>(load_io<C::IO_BF16>(p.v_new, nrow + d), inv_v);
+    char* dst = vpool + toff + v_elem_offset<KV, D, BS>(r16, d);
+    if constexpr (C::ELEM == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)code;
+    else *reinterpret_cast<uint8_t*>(dst) = (uint8_t)code;
+  }
+}
+
 template <int KV, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
   // With events, the start/stop stamps are taken by the dispatch packets of
   // the kernels themselves (ev[0..1] attention, ev[2..3] merge).
-  hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS>), dim3(p.n_waves / 4), dim3(kBlockThreads),
-                        0, stream, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, p,
-                        p.block_tables, p.context_lens, p.positions,
-                        static_cast<char*>(p.k_pool), static_cast<char*>(p.v_pool));
+  if (p.n_qtok > 1) {
+    if constexpr (KV == KV_F32) {
+      return hipErrorInvalidValue;             // several new tokens: bf16 and fp8 caches only
+    } else {
+      const int64_t items = (int64_t)p.batch * p.n_qtok * p.n_kv_heads;
+      hipLaunchKernelGGL((decode_append_kernel<KV, D, BS>),
+                         dim3((unsigned)((items + kBlockThreads / 64 - 1) / (kBlockThreads / 64))),
+                         dim3(kBlockThreads), 0, stream, p);
+      hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, true>), dim3(p.n_waves / 4),
+                            dim3(kBlockThreads), 0, stream, ev ? ev[0] : nullptr,
+                            ev ? ev[1] : nullptr, 0, p, p.block_tables, p.context_lens,
+                            p.positions, static_cast<char*>(p.k_pool),
+                            static_cast<char*>(p.v_pool));
+    }
+  } else {
+    hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, false>), dim3(p.n_waves / 4),
+                          dim3(kBlockThreads), 0, stream, ev ? ev[0] : nullptr,
+                          ev ? ev[1] : nullptr, 0, p, p.block_tables, p.context_lens,
+                          p.positions, static_cast<char*>(p.k_pool),
+                          static_cast<char*>(p.v_pool));
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_merge<KV != KV_F32, D>(p, stream, ev);
@@ -1127,7 +1240,7 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
 
 template <int KV, int D, int BS>
 hipError_t occupancy_typed(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_attn_kernel<KV, D, BS>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_attn_kernel<KV, D, BS, false>,
                                                       kBlockThreads, 0);
 }
 

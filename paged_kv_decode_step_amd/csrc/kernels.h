@@ -50,6 +50,7 @@ struct DecodeParams {
   int32_t weight_min_share;  // units per wavefront below which the weights are even
   float sm_scale_log2;       // log2(e) / sqrt(D)
   int32_t window;            // attention window in tokens (0 = the whole context)
+  int32_t n_qtok;            // new tokens per request (1, or up to 16 / group)
 };
 
 // Floats of one partial softmax state: the accumulator of all 64 lanes

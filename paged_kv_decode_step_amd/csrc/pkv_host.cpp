@@ -412,7 +412,8 @@ pkv_status pkv_check_decode_args(int64_t num_blocks, int32_t block_size, int32_t
 
 static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
                                  const int32_t* block_tables, int32_t max_blocks,
-                                 const int32_t* context_lens, int32_t batch, hipStream_t stream) {
+                                 const int32_t* context_lens, int32_t batch, int32_t n_new,
+                                 hipStream_t stream) {
   std::vector<int32_t> lens(batch), pos(batch), tab((size_t)batch * max_blocks);
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -424,12 +425,12 @@ static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
   const int64_t cap = (int64_t)max_blocks * pool->block_size;
   std::vector<int32_t> last_owner(pool->num_blocks, -1);
   for (int b = 0; b < batch; ++b) {
-    if (lens[b] < 1 || lens[b] > cap)
-      return fail(PKV_ERR_DEVICE_DATA, "context_lens[%d] = %d outside [1, %lld]", b, lens[b],
-                  (long long)cap);
-    if (pos[b] < 0 || pos[b] >= pool->rope_max_pos)
-      return fail(PKV_ERR_DEVICE_DATA, "positions[%d] = %d outside [0, %d)", b, pos[b],
-                  pool->rope_max_pos);
+    if (lens[b] < n_new || lens[b] > cap)
+      return fail(PKV_ERR_DEVICE_DATA, "context_lens[%d] = %d outside [%d, %lld]", b, lens[b],
+                  n_new, (long long)cap);
+    if (pos[b] < 0 || pos[b] + n_new - 1 >= pool->rope_max_pos)
+      return fail(PKV_ERR_DEVICE_DATA, "positions[%d] = %d: new tokens outside [0, %d)", b,
+                  pos[b], pool->rope_max_pos);
     const int nb = (lens[b] + pool->block_size - 1) / pool->block_size;
     for (int j = 0; j < nb; ++j) {
       const int32_t id = tab[(size_t)b * max_blocks + j];
@@ -456,10 +457,49 @@ static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
   return PKV_OK;
 }
 
+static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
+                              const void* v_new, pkv_dtype io_dtype, int32_t n_new,
+                              const int32_t* positions, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t batch, int32_t n_q_heads, void* out, void* stream);
+
 pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
                        pkv_dtype io_dtype, const int32_t* positions, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
                        int32_t n_q_heads, void* out, void* stream) {
+  return launch_step(pool, q, k_new, v_new, io_dtype, 1, positions, block_tables,
+                     max_blocks_per_seq, context_lens, batch, n_q_heads, out, stream);
+}
+
+pkv_status decode_step_multi(pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
+                             pkv_dtype io_dtype, int32_t n_new, const int32_t* positions,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t batch, int32_t n_q_heads,
+                             void* out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (n_new < 1) return fail(PKV_ERR_INVALID, "n_new must be >= 1");
+  if (n_new > 1) {
+    if (pool->kv_dtype == PKV_F32)
+      return fail(PKV_ERR_UNSUPPORTED, "several new tokens need a bf16 or fp8 cache");
+    if (pool->window > 0)
+      return fail(PKV_ERR_UNSUPPORTED, "several new tokens with an attention window");
+    if (n_q_heads >= pool->n_kv_heads && n_q_heads % pool->n_kv_heads == 0 &&
+        (int64_t)(n_q_heads / pool->n_kv_heads) * n_new > pkv::kGroupMax)
+      return fail(PKV_ERR_UNSUPPORTED, "group (%d) x new tokens (%d) above %d",
+                  n_q_heads / pool->n_kv_heads, n_new, pkv::kGroupMax);
+    if (pool->rope_max_pos >= 1 && pool->rope_max_pos < n_new)
+      return fail(PKV_ERR_INVALID, "RoPE table of %d positions for %d new tokens",
+                  pool->rope_max_pos, n_new);
+  }
+  return launch_step(pool, q, k_new, v_new, io_dtype, n_new, positions, block_tables,
+                     max_blocks_per_seq, context_lens, batch, n_q_heads, out, stream);
+}
+
+static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
+                              const void* v_new, pkv_dtype io_dtype, int32_t n_new,
+                              const int32_t* positions, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t batch, int32_t n_q_heads, void* out, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
   pkv_status s = pkv_check_decode_args(pool->num_blocks, pool->block_size, pool->n_kv_heads,
                                        pool->head_dim, pool->kv_dtype, io_dtype, q, k_new, v_new,
@@ -472,7 +512,8 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
     return fail(PKV_ERR_STATE, "kv_pool_set_fp8_scales was not called");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (env_int("PKV_DEBUG", 0) == 1) {
-    s = debug_validate(pool, positions, block_tables, max_blocks_per_seq, context_lens, batch, st);
+    s = debug_validate(pool, positions, block_tables, max_blocks_per_seq, context_lens, batch,
+                       n_new, st);
     if (s != PKV_OK) return s;
   }
   pkv::DecodeParams p;
@@ -509,6 +550,7 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const v
   p.weight_min_share = pkv::kWeightMinShare;
   p.sm_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)pool->head_dim));
   p.window = pool->window;
+  p.n_qtok = n_new;
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
     const size_t need = 4 * (size_t)(pool->timed_calls + 1);
