@@ -35,7 +35,7 @@ METRIC = "paged decode attention: HBM GB/s (% of peak) and decode tokens/s per l
 ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
-def algorithmic_bytes(wl, window: int = 0) -> int:
+def algorithmic_bytes(wl, window: int = 0, new_tokens: int = 1) -> int:
     """Bytes the step must move: cached K/V read once per KV head, the new
     K/V written, q/k_new/v_new read, out written, the block-table entries,
     positions and lengths, the RoPE rows and (fp8) the scales.  With an
@@ -49,11 +49,12 @@ def algorithmic_bytes(wl, window: int = 0) -> int:
     if window > 0:
         first = np.maximum(L - window, 0)
     per_tok = 2 * c.n_kv_heads * c.head_dim * s_kv
-    total = int(((L - first - 1) * per_tok).sum())               # read cached K, V
-    total += wl.batch * per_tok                                  # write new K, V
-    total += wl.batch * (2 * c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * s_io
+    T = new_tokens
+    total = int(((L - first - T) * per_tok).sum())               # read cached K, V
+    total += wl.batch * T * per_tok                              # write new K, V
+    total += wl.batch * T * (2 * c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * s_io
     total += int((4 * ((L + bs - 1) // bs - first // bs) + 8).sum())
-    total += wl.batch * c.head_dim * 4                           # cos + sin rows
+    total += wl.batch * T * c.head_dim * 4                       # cos + sin rows
     if c.kv_dtype == "fp8":
         total += 16 * c.n_kv_heads
     return total
@@ -284,6 +285,8 @@ def main():
     ap.add_argument("--min-cold-bytes", type=float, default=1.0e9)
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention over the last W tokens (0 = whole context)")
+    ap.add_argument("--new-tokens", type=int, default=1,
+                    help="T new tokens per request (decode_step_multi; the lengths count them)")
     ap.add_argument("--allocator", action="store_true",
                     help="only measure the block allocator's host step (prepare_step for the "
                          "workload's batch) and the device block copy, one JSON line")
@@ -317,7 +320,7 @@ def main():
     if args.allocator:
         print(json.dumps(allocator_bench(wl, device, args.steps)), flush=True)
         return
-    alg = algorithmic_bytes(wl, args.window)
+    alg = algorithmic_bytes(wl, args.window, args.new_tokens)
     kv_bytes = int(((wl.context_lens.astype(np.int64)) * 2 * c.n_kv_heads * c.head_dim
                     * ELEM[c.kv_dtype]).sum())
     n_layers = max(1, math.ceil(args.min_cold_bytes / (min(kv_bytes, alg) if args.window else kv_bytes)))
@@ -328,7 +331,21 @@ def main():
           f"{n_layers} pool copies, {pools[0].info()['n_waves']} wavefronts", file=sys.stderr,
           flush=True)
 
+    T = args.new_tokens
+    if T > 1:
+        # T new tokens per request: [B, T, H, D] inputs; positions of the first new token
+        dt = t["q"].dtype
+        gen = torch.Generator(device=device).manual_seed(1234)
+        for w, h in (("q", c.n_q_heads), ("k_new", c.n_kv_heads), ("v_new", c.n_kv_heads)):
+            t[w] = torch.randn(wl.batch, T, h, c.head_dim, device=device, generator=gen).to(dt)
+        t["out"] = torch.empty_like(t["q"])
+        t["positions"] = (t["context_lens"] - T).contiguous()
+
     def step(i):
+        if T > 1:
+            pkv.decode_step_multi(pools[i % n_layers], t["q"], t["k_new"], t["v_new"],
+                                  t["positions"], t["block_tables"], t["context_lens"], t["out"])
+            return
         pkv.decode_step(pools[i % n_layers], t["q"], t["k_new"], t["v_new"], t["positions"],
                         t["block_tables"], t["context_lens"], t["out"])
 
@@ -412,9 +429,10 @@ def main():
                    "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
                    "block_size": c.block_size, "kv_dtype": c.kv_dtype,
                    "io_dtype": c.io_dtype, "mean_context": float(wl.context_lens.mean()),
-                   "pool_copies": n_layers, "window": args.window},
+                   "pool_copies": n_layers, "window": args.window,
+                   "new_tokens": args.new_tokens},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "tokens_per_s_per_layer": round(wl.batch / (ms_per_step * 1e-3), 1),
+        "tokens_per_s_per_layer": round(wl.batch * T / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,
         "kernel_ms": {"attention": round(attn_avg, 5), "merge": round(merge_avg, 5)},
         "graph": None if graph_ms is None else {
@@ -428,7 +446,7 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and T == 1:
         result["cpu_baseline"] = cpu_baseline(wl, pools[0], t, scales, args.cpu_budget,
                                               args.window)
     for p in pools:
