@@ -438,11 +438,15 @@ static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
         return fail(PKV_ERR_DEVICE_DATA, "block_tables[%d][%d] = %d outside [0, %lld)", b, j, id,
                     (long long)pool->num_blocks);
     }
-    const int32_t lb = tab[(size_t)b * max_blocks + nb - 1];
-    if (last_owner[lb] >= 0)
-      return fail(PKV_ERR_DEVICE_DATA,
-                  "block %d receives the new token of requests %d and %d", lb, last_owner[lb], b);
-    last_owner[lb] = b;
+    // every block that receives one of the request's new tokens
+    const int j0 = (lens[b] - n_new) / pool->block_size;
+    for (int j = j0; j < nb; ++j) {
+      const int32_t lb = tab[(size_t)b * max_blocks + j];
+      if (last_owner[lb] >= 0 && last_owner[lb] != b)
+        return fail(PKV_ERR_DEVICE_DATA,
+                    "block %d receives new tokens of requests %d and %d", lb, last_owner[lb], b);
+      last_owner[lb] = b;
+    }
   }
   for (int b = 0; b < batch; ++b) {   // the appended block must not be read by others
     const int nb = (lens[b] + pool->block_size - 1) / pool->block_size;
