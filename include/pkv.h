@@ -25,6 +25,11 @@
  *     "4. Native FP8 Quantization on NVIDIA Hopper & Blackwell" (here one
  *     fp32 scale per KV head for K and one for V).
  *
+ * Around the step: several new tokens per request (decode_step_multi), a
+ * sliding attention window (kv_pool_set_window), whole-block copies for copy
+ * on write (kv_pool_copy_blocks) and a host block allocator (pkv_alloc_*,
+ * pkv_seq_*); each declaration below cites the passage it follows.
+ *
  * Conventions.  All sizes are element counts unless named *_bytes.  Device
  * pointers are HIP device addresses on the pool's device.  Every function
  * returns a pkv_status and never throws; on failure pkv_last_error() returns a
