@@ -422,19 +422,23 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   Walk w0;
   int T;
   {
-    const TilePos t0 = tile_at_unit(sP, B, hkv, cost, wave_start(wave, U, W, ww));
-    const int64_t g0 = global_tile(sP, t0.b, t0.h, t0.j, t0.n, hkv, cost);
-    const int64_t x1 = wave_start(wave + 1, U, W, ww);
-    int64_t g1 = (int64_t)sP[B] - (int64_t)hkv * cost * B;       // all tiles
-    if (x1 < U) {
-      const TilePos t1 = tile_at_unit(sP, B, hkv, cost, x1);
-      g1 = global_tile(sP, t1.b, t1.h, t1.j, t1.n, hkv, cost);
+    // Even lanes work out where the range starts and odd lanes where it ends
+    // (the next wavefront's start), side by side in one instruction stream.
+    const int end = lane & 1;
+    const int64_t x = wave_start(wave + end, U, W, ww);
+    int64_t g = (int64_t)sP[B] - (int64_t)hkv * cost * B;        // all tiles
+    TilePos t = {0, 0, 0, 1};
+    if (x < U) {
+      t = tile_at_unit(sP, B, hkv, cost, x);
+      g = global_tile(sP, t.b, t.h, t.j, t.n, hkv, cost);
     }
-    T = uniform((int)(g1 - g0));
-    w0.b = uniform(t0.b);
-    w0.h = uniform(t0.h);
-    w0.j = uniform(t0.j);
-    w0.n = uniform(t0.n);
+    const int g0 = __builtin_amdgcn_readlane((int)g, 0);     // tile counts < 2^31
+    const int g1 = __builtin_amdgcn_readlane((int)g, 1);
+    T = g1 - g0;
+    w0.b = __builtin_amdgcn_readlane(t.b, 0);
+    w0.h = __builtin_amdgcn_readlane(t.h, 0);
+    w0.j = __builtin_amdgcn_readlane(t.j, 0);
+    w0.n = __builtin_amdgcn_readlane(t.n, 0);
     if (T > 0 && w0.j == w0.n) {        // the range begins at the next sequence
       w0.j = 0;
       if (++w0.h == hkv) {
