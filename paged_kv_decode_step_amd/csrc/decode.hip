@@ -1042,13 +1042,19 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
   constexpr int PF = partial_floats(D);
   constexpr int PPB = 32 / KC;                  // pieces per batch
   const int lane = threadIdx.x & 63;
-  const int w = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
+  const int G = p.group, hkv = p.n_kv_heads, TQ = p.n_qtok;
+  // With several new tokens per request, merge wavefront mw takes the G
+  // columns of new token qi = mw % TQ of the sequence whose header
+  // wavefront mw / TQ left, so each merges G columns as with one token.
+  const int mw = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
+  const int w = TQ > 1 ? mw / TQ : mw;
+  const int qi = TQ > 1 ? mw - w * TQ : 0;
   const int4 hdr = p.headers[w];
   if (!uniform(hdr.x)) return;
-  const int G = p.group, hkv = p.n_kv_heads, TQ = p.n_qtok;
   const int seq = uniform(hdr.y), np = uniform(hdr.z), slot0 = uniform(hdr.w);
   const int b = seq / hkv, h = seq - (seq / hkv) * hkv;
-  const int nchunk = G * TQ * D / 4;          // columns (query head g of new token qi) x D
+  const int nchunk = G * D / 4;               // query head x D of new token qi
+  const int cbase = qi * nchunk;              // its first chunk in a piece
   int ch[KC], hd[KC];
   bool ok[KC];
   float M[KC], den[KC];
@@ -1071,8 +1077,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
       const float* part = p.partials + ((int64_t)(w + pc) * 2 + (pc == 0 ? slot0 : 0)) * PF;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
-        a[j][k] = ok[k] ? *reinterpret_cast<const f32x4_t*>(part + 4 * ch[k]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        ml[j][k] = *reinterpret_cast<const f32x2_t*>(part + 16 * D + 2 * hd[k]);
+        a[j][k] = ok[k] ? *reinterpret_cast<const f32x4_t*>(part + 4 * (cbase + ch[k]))
+                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ml[j][k] = *reinterpret_cast<const f32x2_t*>(part + 16 * D + 2 * (qi * G + hd[k]));
       }
     }
 #pragma unroll
@@ -1101,8 +1108,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
     if (!ok[k]) continue;
     const float inv = den[k] > 0.f ? 1.0f / den[k] : 0.f;
     const int d = 4 * ch[k] - hd[k] * D;
-    const int qi = TQ > 1 ? hd[k] / G : 0;     // new token of the column
-    const int64_t row = (((int64_t)b * TQ + qi) * hkv * G + h * G + (hd[k] - qi * G)) * D;
+    const int64_t row = (((int64_t)b * TQ + qi) * hkv * G + h * G + hd[k]) * D;
     if constexpr (IO_BF16) {
       u32x2_t o;
       o[0] = bf16_rne(num[k][0] * inv) | (bf16_rne(num[k][1] * inv) << 16);
@@ -1118,8 +1124,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
 // two >= G*D / 256.
 template <bool IO_BF16, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
-  const int need = (p.group * p.n_qtok * D / 4 + 63) / 64;
-  const dim3 grid(p.n_waves / 4), block(kBlockThreads);
+  const int need = (p.group * D / 4 + 63) / 64;
+  const dim3 grid(p.n_waves / 4 * p.n_qtok), block(kBlockThreads);
   hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
   if (need <= 1) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 1>), grid, block, 0, stream, e0, e1, 0, p);
   else if (need <= 2) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 2>), grid, block, 0, stream, e0, e1, 0, p);
