@@ -522,16 +522,16 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 
   enum : uint32_t { Q_OUT = 0, Q_APPEND = 1, Q_PART = 2 };
   constexpr int IO_BYTES = C::IO_BF16 ? 2 : 4;
-  const int out_words = G * D * IO_BYTES / 16;            // G output rows
+  const int out_words = NC * D * IO_BYTES / 16;           // G output rows per new token
   constexpr int app_words = C::KROWS + D / 4;             // key row + value codes (u32)
-  const int part_words = G * D / 4 + (G + 1) / 2;         // [head][dim] accumulators + (m, l)
+  const int part_words = NC * D / 4 + (NC + 1) / 2;       // [column][dim] accumulators + (m, l)
   int q_used = 0;      // words of sQ[wid] in use
   uint32_t* const sQw = reinterpret_cast<uint32_t*>(&sQ[wid][0]);
 
   // Room for an item of `words` payload words: the word index of its
   // header, or -1 (the write is then made at once).
   auto q_reserve = [&](int words) __attribute__((always_inline)) -> int {
-    if (MQ || q_used + 1 + words > QW) return -1;
+    if (q_used + 1 + words > QW) return -1;
     const int at = q_used;
     q_used += 1 + words;
     return at;
@@ -933,12 +933,12 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     const int at = slot == 0 ? q_reserve(part_words) : -1;
     if (at >= 0) {
       q_header(at, Q_PART, part_words, cw.b * hkv + cw.h, 0, 0);
-      if (lr < G) {
+      if (lr < NC) {
         f32x4_t* accq = reinterpret_cast<f32x4_t*>(&sQ[wid][at + 1]);
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) accq[(lr * D + 16 * nt + 4 * lq) / 4] = acc[nt] * vsc;
         if (lq == 0) {
-          float* ml = reinterpret_cast<float*>(&sQ[wid][at + 1 + G * D / 4]);
+          float* ml = reinterpret_cast<float*>(&sQ[wid][at + 1 + NC * D / 4]);
           ml[2 * lr] = m_run;
           ml[2 * lr + 1] = lt;
         }
@@ -995,16 +995,22 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     const int b = seq / hkv, h = seq - b * hkv;
     const u32x4_t* pl = &sQ[wid][off + 1];
     if (type == Q_OUT) {
-      char* dst = static_cast<char*>(p.out) + ((int64_t)b * out_row_stride + h * G) * D * IO_BYTES;
-      for (int w = lane; w < words; w += 64) *reinterpret_cast<u32x4_t*>(dst + (int64_t)w * 16) = pl[w];
+      // the G rows of each new token are contiguous in `out`
+      const int seg = words / TQ;
+      for (int qi = 0; qi < TQ; ++qi) {
+        char* dst = static_cast<char*>(p.out) +
+                    (((int64_t)b * TQ + qi) * out_row_stride + h * G) * D * IO_BYTES;
+        for (int w = lane; w < seg; w += 64)
+          *reinterpret_cast<u32x4_t*>(dst + (int64_t)w * 16) = pl[qi * seg + w];
+      }
     } else if (type == Q_APPEND) {
       write_append(h, uniform((int)hd[2]), uniform((int)hd[3]), pl,
                    reinterpret_cast<const uint32_t*>(pl + C::KROWS));
     } else {                                   // partial state of the first piece (slot 0)
       float* part = p.partials + (int64_t)wave * 2 * PF;
-      for (int w = lane; w < G * D / 4; w += 64) *reinterpret_cast<u32x4_t*>(part + 4 * w) = pl[w];
-      if (lane < G) {
-        const float* ml = reinterpret_cast<const float*>(pl + G * D / 4);
+      for (int w = lane; w < NC * D / 4; w += 64) *reinterpret_cast<u32x4_t*>(part + 4 * w) = pl[w];
+      if (lane < NC) {
+        const float* ml = reinterpret_cast<const float*>(pl + NC * D / 4);
         part[16 * D + 2 * lane] = ml[2 * lane];
         part[16 * D + 2 * lane + 1] = ml[2 * lane + 1];
       }
