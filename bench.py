@@ -385,29 +385,33 @@ def main():
 
     # the same steps replayed from one HIP graph that records a step on every
     # pool copy: a multi-layer decode step issued with a single launch
-    graph_ms = None
+    graph_ms, graph_error = None, None
     if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(n_layers):
-                step(i)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n_layers):
-                step(i)
-        reps = max(1, args.steps // n_layers)
-        graph.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for i in range(n_layers):
+                    step(i)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(n_layers):
+                    step(i)
+            reps = max(1, args.steps // n_layers)
             graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / (reps * n_layers)
-        del graph
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / (reps * n_layers)
+            del graph
+        except Exception as exc:   # the graph figure is optional; the eager line stands
+            graph_error = f"{type(exc).__name__}: {exc}"
+            torch.cuda.synchronize()
 
     gbs = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (attn_avg * 1e-3) / 1e9
@@ -435,7 +439,7 @@ def main():
         "tokens_per_s_per_layer": round(wl.batch * T / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,
         "kernel_ms": {"attention": round(attn_avg, 5), "merge": round(merge_avg, 5)},
-        "graph": None if graph_ms is None else {
+        "graph": ({"error": graph_error} if graph_error else None) if graph_ms is None else {
             "layers": n_layers, "ms_per_step": round(graph_ms, 5),
             "GB/s": round(alg / (graph_ms * 1e-3) / 1e9, 2),
             "note": "one HIP graph replays a step on each pool copy (a multi-layer step); "
