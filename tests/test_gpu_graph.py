@@ -74,3 +74,60 @@ def test_multi_layer_step_replayed_from_a_graph(kv):
     finally:
         for r in runs:
             r.close()
+
+
+@pytest.mark.parametrize("mode", ["window", "multi"])
+def test_windowed_and_multi_token_steps_replay_from_a_graph(mode):
+    """The windowed step and the multi-token step (its append launch, the
+    attention and the merge) record into a graph too; every replay gives the
+    eager outputs and pools bit for bit."""
+    lens = [5, 37, 200, 513, 1000]
+    wl = workloads.custom_workload(lens, n_q_heads=16, n_kv_heads=4, head_dim=128, block_size=16,
+                                   kv_dtype="bf16", io_dtype="bf16", rope_theta=5.0e5, seed=77)
+    arrs = problem.build(wl)
+    run = gp.Run(wl, arrs, max_position=2048)
+    try:
+        rng = np.random.default_rng(77)
+        if mode == "window":
+            run.pool.set_window(100)
+
+            def launch():
+                pkv.decode_step(run.pool, run.q, run.k_new, run.v_new, run.positions, run.tables,
+                                run.lens, run.out)
+            out = run.out
+        else:
+            tq, b = 3, len(lens)
+            enc = lambda shape: gp.io_to_torch(
+                problem.encode_io(rng.standard_normal(shape).astype(np.float32), "bf16"), "bf16")
+            q, kn, vn = enc((b, tq, 16, 128)), enc((b, tq, 4, 128)), enc((b, tq, 4, 128))
+            pos = (run.lens - tq).contiguous()
+            out = torch.full_like(q, float("nan"))
+
+            def launch():
+                pkv.decode_step_multi(run.pool, q, kn, vn, pos, run.tables, run.lens, out)
+        launch()
+        torch.cuda.synchronize()
+        eager_out = out.clone()
+        eager_pools = run.pools()
+        assert torch.isfinite(eager_out.float()).all()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            launch()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch()
+        for rep in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager_out.view(torch.int16)), rep
+            kp, vp = run.pools()
+            assert np.array_equal(gp.bits(kp), gp.bits(eager_pools[0]))
+            assert np.array_equal(gp.bits(vp), gp.bits(eager_pools[1]))
+        assert run.pool.device_errors() == 0
+    finally:
+        run.close()

@@ -8,6 +8,7 @@ import pytest
 
 import gpu_problem as gp
 import oracle
+import paged_kv_decode_step_amd as pkv
 import problem
 import workloads
 from problem import NAN_CODE
@@ -60,3 +61,15 @@ def test_window_matches_the_oracle(kv, d, bs, window):
             assert run.pool.device_errors() == 0
         finally:
             run.close()
+
+
+def test_negative_window_is_refused():
+    wl, arrs, _ = windowed_case("bf16", 128, 16, 7, seed=99)
+    run = gp.Run(wl, arrs)
+    try:
+        with pytest.raises(pkv.PkvError) as e:
+            run.pool.set_window(-1)
+        assert e.value.status == -1
+        assert run.pool.info()["window"] == 0
+    finally:
+        run.close()
