@@ -164,6 +164,15 @@ def test_batch_zero_is_a_noop():
     pool.close()
 
 
+def test_largest_batch():
+    """4096 requests (the most one step takes, every slot of the per-request
+    prefix array in use) with short ragged contexts of 1..70 tokens."""
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 71, 4096)]
+    wl = small(lens, hq=4, hkv=2, d=64, seed=41)
+    run_and_check(wl)
+
+
 def test_missing_rope_table_is_a_state_error():
     pool = pkv.KVPool(4, 16, 2, 64, "bf16")
     q = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device="cuda")
