@@ -34,7 +34,9 @@
  * pointers are HIP device addresses on the pool's device.  Every function
  * returns a pkv_status and never throws; on failure pkv_last_error() returns a
  * thread-local message.  Host-visible arguments are checked before any HIP
- * call.
+ * call.  Calls that take a stream refuse (PKV_ERR_INVALID) one that is not on
+ * the pool's device; NULL is the current device's default stream.  Calls
+ * that allocate do so on the pool's device, whichever device is current.
  */
 #ifndef PKV_H_
 #define PKV_H_

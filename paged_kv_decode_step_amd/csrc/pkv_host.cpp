@@ -125,6 +125,20 @@ struct pkv_pool {
 
 static constexpr int kMaxTimedCalls = 65536;
 
+// Makes `device` current for its lifetime and restores the caller's device.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int device) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    (void)hipSetDevice(device);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+  DeviceGuard(const DeviceGuard&) = delete;
+  DeviceGuard& operator=(const DeviceGuard&) = delete;
+};
+
 static void free_pool(pkv_pool* p) {
   if (!p) return;
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
@@ -247,12 +261,9 @@ pkv_status kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t n_kv_h
 
 pkv_status kv_pool_destroy(pkv_pool* pool) {
   if (!pool) return PKV_OK;
-  int cur = 0;
-  (void)hipGetDevice(&cur);
-  (void)hipSetDevice(pool->device);
+  DeviceGuard g(pool->device);
   (void)hipDeviceSynchronize();
   free_pool(pool);
-  (void)hipSetDevice(cur);
   return PKV_OK;
 }
 
@@ -264,6 +275,7 @@ pkv_status kv_pool_set_rope(pkv_pool* pool, double theta, int32_t max_position) 
   std::vector<float> c(n), s(n);
   pkv_status st = pkv_rope_table_host(theta, pool->head_dim, max_position, c.data(), s.data());
   if (st != PKV_OK) return st;
+  DeviceGuard g(pool->device);
   (void)hipFree(pool->rope_cos);
   (void)hipFree(pool->rope_sin);
   pool->rope_cos = pool->rope_sin = nullptr;
@@ -349,12 +361,12 @@ pkv_status kv_pool_set_tuning(pkv_pool* pool, int32_t waves_per_cu, int32_t min_
     return fail(PKV_ERR_INVALID, "odd_weight_pct must be -1 (automatic) or in [1, 100]");
   if (waves_per_cu < 0 || waves_per_cu > 32)
     return fail(PKV_ERR_INVALID, "waves_per_cu must be in [0, 32]");
-  int cur = 0;
-  (void)hipGetDevice(&cur);
-  (void)hipSetDevice(pool->device);
-  (void)hipDeviceSynchronize();
-  pkv_status s = size_workspace(pool, waves_per_cu);
-  (void)hipSetDevice(cur);
+  pkv_status s;
+  {
+    DeviceGuard g(pool->device);
+    (void)hipDeviceSynchronize();
+    s = size_workspace(pool, waves_per_cu);
+  }
   if (s != PKV_OK) return s;
   pool->min_units = min_units;
   pool->piece_cost = resolve_piece_cost(piece_cost, pool->ring_tiles);
@@ -461,6 +473,19 @@ static pkv_status debug_validate(const pkv_pool* pool, const int32_t* positions,
   return PKV_OK;
 }
 
+// Work for a pool goes on a stream of the pool's device (NULL: the current
+// device's default stream); a kernel on another device would read this
+// device's memory from there.
+static pkv_status check_stream_device(const pkv_pool* pool, hipStream_t st) {
+  int dev = -1;
+  const hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  if (dev != pool->device)
+    return fail(PKV_ERR_INVALID, "stream is on device %d, the pool on device %d", dev,
+                pool->device);
+  return PKV_OK;
+}
+
 static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
                               const void* v_new, pkv_dtype io_dtype, int32_t n_new,
                               const int32_t* positions, const int32_t* block_tables,
@@ -515,6 +540,8 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   if (pool->kv_dtype == PKV_FP8_E4M3 && !pool->has_scales)
     return fail(PKV_ERR_STATE, "kv_pool_set_fp8_scales was not called");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  s = check_stream_device(pool, st);
+  if (s != PKV_OK) return s;
   if (env_int("PKV_DEBUG", 0) == 1) {
     s = debug_validate(pool, positions, block_tables, max_blocks_per_seq, context_lens, batch,
                        n_new, st);
@@ -558,6 +585,7 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   hipEvent_t* ev = nullptr;
   if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
     const size_t need = 4 * (size_t)(pool->timed_calls + 1);
+    DeviceGuard g(pool->device);
     while (pool->events.size() < need) {
       hipEvent_t e;
       hipError_t he = hipEventCreate(&e);
@@ -586,6 +614,8 @@ pkv_status kv_pool_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_p
   if (n_pairs < 0) return fail(PKV_ERR_INVALID, "n_pairs must be >= 0");
   if (n_pairs == 0) return PKV_OK;
   if (!pairs) return fail(PKV_ERR_INVALID, "pairs is null");
+  const pkv_status s = check_stream_device(pool, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
   const hipError_t e = pkv::launch_copy_blocks(pairs, n_pairs, pool->kv_bytes / pool->num_blocks,
                                                (int32_t)pool->num_blocks, pool->k, pool->v,
                                                pool->err, static_cast<hipStream_t>(stream));
@@ -625,6 +655,7 @@ pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms
 pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags) {
   if (!pool || !flags) return fail(PKV_ERR_INVALID, "null argument");
   uint32_t f[4] = {0, 0, 0, 0};
+  DeviceGuard g(pool->device);
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(f, pool->err, sizeof f, hipMemcpyDeviceToHost);
   if (e == hipSuccess) e = hipMemset(pool->err, 0, sizeof f);
