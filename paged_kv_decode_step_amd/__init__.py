@@ -154,6 +154,7 @@ class KVPool:
         self._h = h
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.n_kv_heads, self.head_dim = int(n_kv_heads), int(head_dim)
+        self.device = int(self.info()["device"])      # HIP ordinal the pool lives on
 
     @property
     def handle(self):
@@ -183,8 +184,9 @@ class KVPool:
     def copy_blocks(self, pairs, stream=None) -> None:
         """Copy whole blocks, ``pairs`` an int32 ``[n, 2]`` device tensor of
         (source, destination) ids (``kv_pool_copy_blocks``; asynchronous)."""
-        if pairs.dtype != torch.int32 or not pairs.is_contiguous() or pairs.device.type != "cuda":
-            raise PkvError(-1, "pairs must be a contiguous int32 GPU tensor")
+        if (pairs.dtype != torch.int32 or not pairs.is_contiguous() or pairs.device.type != "cuda"
+                or pairs.device.index != self.device):
+            raise PkvError(-1, f"pairs must be a contiguous int32 tensor on cuda:{self.device}")
         if pairs.dim() != 2 or pairs.shape[1] != 2:
             raise PkvError(-1, "pairs must be [n, 2]")
         if stream is None:
@@ -263,8 +265,8 @@ def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
                     ("context_lens", context_lens)):
         if not t.is_contiguous():
             raise PkvError(-1, f"{name} must be contiguous")
-        if t.device.type != "cuda":
-            raise PkvError(-1, f"{name} must be on the GPU")
+        if t.device.type != "cuda" or t.device.index != pool.device:
+            raise PkvError(-1, f"{name} must be on the pool's GPU (cuda:{pool.device})")
     for name, t in (("positions", positions), ("block_tables", block_tables),
                     ("context_lens", context_lens)):
         if t.dtype != torch.int32:
@@ -394,8 +396,8 @@ def decode_step_multi(pool: KVPool, q, k_new, v_new, positions, block_tables,
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("out", out),
                     ("positions", positions), ("block_tables", block_tables),
                     ("context_lens", context_lens)):
-        if not t.is_contiguous() or t.device.type != "cuda":
-            raise PkvError(-1, f"{name} must be contiguous on the GPU")
+        if not t.is_contiguous() or t.device.type != "cuda" or t.device.index != pool.device:
+            raise PkvError(-1, f"{name} must be contiguous on the pool's GPU (cuda:{pool.device})")
     for name, t in (("positions", positions), ("block_tables", block_tables),
                     ("context_lens", context_lens)):
         if t.dtype != torch.int32:

@@ -164,6 +164,28 @@ def test_batch_zero_is_a_noop():
     pool.close()
 
 
+def test_tensors_off_the_pool_device_are_refused():
+    pool = pkv.KVPool(4, 16, 2, 64, "bf16")
+    pool.set_rope(1e4, 8)
+    assert pool.device == torch.cuda.current_device()
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device="cuda")
+    kn = torch.zeros(1, 2, 64, dtype=torch.bfloat16, device="cuda")
+    one = torch.ones(1, dtype=torch.int32, device="cuda")
+    tab = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.decode_step(pool, q.cpu(), kn, kn, one - 1, tab, one, torch.empty_like(q))
+    assert e.value.status == -1
+    with pytest.raises(pkv.PkvError) as e:
+        pool.copy_blocks(torch.tensor([[0, 1]], dtype=torch.int32))
+    assert e.value.status == -1
+    out = torch.empty_like(q)
+    pkv.decode_step(pool, q, kn, kn, one - 1, tab, one, out)   # the same step on the device runs
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert pool.device_errors() == 0
+    pool.close()
+
+
 def test_largest_batch():
     """4096 requests (the most one step takes, every slot of the per-request
     prefix array in use) with short ragged contexts of 1..70 tokens."""
