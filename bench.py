@@ -240,10 +240,13 @@ def allocator_bench(wl, device, steps: int) -> dict:
     seqs = [alloc.add(int(L) - 1) for L in lens]
     reps, t_host = max(1, min(steps, 50)), 0.0
     maxb = int(wl.block_tables.shape[1]) + (reps + 2) // c.block_size + 2
-    alloc.prepare_step(seqs, maxb)          # first touch of the host arrays
+    # the host arrays a serving loop keeps from step to step
+    bufs = (np.empty((len(seqs), maxb), np.int32), np.empty(len(seqs), np.int32),
+            np.empty(len(seqs), np.int32), np.empty((len(seqs), 2), np.int32))
+    alloc.prepare_step(seqs, maxb, out=bufs)          # first touch of the host arrays
     for _ in range(reps):
         t0 = time.perf_counter()
-        alloc.prepare_step(seqs, maxb)
+        alloc.prepare_step(seqs, maxb, out=bufs)
         t_host += time.perf_counter() - t0
     # copy on write: fork every other request, then one step copies each
     # shared half-full block once

@@ -362,22 +362,40 @@ class BlockAllocator:
                                  nb.value))
         return length.value, [int(b) for b in blocks[:nb.value]]
 
-    def prepare_step(self, seq_ids, max_blocks_per_seq: int, max_copies: int = None):
+    def prepare_step(self, seq_ids, max_blocks_per_seq: int, max_copies: int = None,
+                     out=None):
         """Grow each sequence by one token: (block_tables [B, max_blocks_per_seq],
-        context_lens [B], positions [B], copies [n, 2]), int32 numpy arrays."""
+        context_lens [B], positions [B], copies [n, 2]), int32 numpy arrays.
+
+        ``out``: optional (tables, lens, pos, copies) C-contiguous int32 arrays
+        of at least [B, max_blocks_per_seq], [B], [B] and [max_copies, 2] to
+        fill instead of new ones (a serving loop reuses them every step); the
+        results are views of them."""
         import numpy as np
 
         ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
         b = int(ids.shape[0])
         mc = b if max_copies is None else int(max_copies)
-        tables = np.zeros((max(b, 1), int(max_blocks_per_seq)), dtype=np.int32)
-        lens = np.zeros(max(b, 1), dtype=np.int32)
-        pos = np.zeros(max(b, 1), dtype=np.int32)
-        copies = np.zeros((max(mc, 1), 2), dtype=np.int32)
+        maxb = int(max_blocks_per_seq)
+        if out is None:
+            tables = np.empty((max(b, 1), maxb), dtype=np.int32)
+            lens = np.empty(max(b, 1), dtype=np.int32)
+            pos = np.empty(max(b, 1), dtype=np.int32)
+            copies = np.empty((max(mc, 1), 2), dtype=np.int32)
+        else:
+            tables, lens, pos, copies = out
+            for name, a, ndim in (("tables", tables, 2), ("lens", lens, 1), ("pos", pos, 1),
+                                  ("copies", copies, 2)):
+                if (not isinstance(a, np.ndarray) or a.dtype != np.int32 or a.ndim != ndim
+                        or not a.flags["C_CONTIGUOUS"]):
+                    raise PkvError(-1, f"out {name} must be a C-contiguous int32 array of {ndim} dims")
+            if (tables.shape[0] < b or tables.shape[1] != maxb or lens.shape[0] < b
+                    or pos.shape[0] < b or copies.shape[0] < mc or copies.shape[1] != 2):
+                raise PkvError(-1, "out arrays are too small for this step")
         n = ctypes.c_int32()
         ip = ctypes.POINTER(ctypes.c_int32)
         _check(_lib.pkv_alloc_prepare_step(self.handle, ids.ctypes.data_as(ip), b,
-                                           int(max_blocks_per_seq), tables.ctypes.data_as(ip),
+                                           maxb, tables.ctypes.data_as(ip),
                                            lens.ctypes.data_as(ip), pos.ctypes.data_as(ip),
                                            copies.ctypes.data_as(ip), mc, ctypes.byref(n)))
         return tables[:b], lens[:b], pos[:b], copies[:n.value]

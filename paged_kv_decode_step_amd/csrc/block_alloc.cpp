@@ -243,7 +243,8 @@ pkv_status pkv_alloc_prepare_step(pkv_block_alloc* a, const int32_t* seq_ids, in
     q.len = (int32_t)(slot + 1);
     int32_t* row = block_tables + (int64_t)i * max_blocks_per_seq;
     const int32_t nb = (int32_t)q.blocks.size();
-    for (int32_t j = 0; j < max_blocks_per_seq; ++j) row[j] = j < nb ? q.blocks[(size_t)j] : -1;
+    std::copy(q.blocks.begin(), q.blocks.end(), row);
+    std::fill(row + nb, row + max_blocks_per_seq, -1);
     context_lens[i] = q.len;
     positions[i] = q.len - 1;
   }

@@ -261,3 +261,28 @@ def test_dense_histories_equal_decode_step_on_a_paged_layout(kv, io):
     for s in range(len(lens)):
         np.testing.assert_array_equal(hist.k[s][:, -1], paged["k_app"][s])
         np.testing.assert_array_equal(hist.v[s][:, -1], paged["v_app"][s])
+
+
+def test_prepare_step_into_reused_buffers():
+    """``out=`` fills caller-owned arrays with exactly what fresh arrays get,
+    step after step (stale contents from a longer earlier batch included)."""
+    bs, maxb = 4, 6
+    a = pkv.BlockAllocator(64, bs, 8)
+    b = pkv.BlockAllocator(64, bs, 8)
+    for n in (3, 8, 0, 5):
+        assert a.add(n) == b.add(n)
+    bufs = (np.full((4, maxb), 77, np.int32), np.full(4, 77, np.int32),
+            np.full(4, 77, np.int32), np.full((4, 2), 77, np.int32))
+    for ids in ([0, 1, 2, 3], [3, 1], [2], [0, 1, 2, 3]):
+        got = a.prepare_step(ids, maxb, out=bufs)
+        want = b.prepare_step(ids, maxb)
+        for g, w in zip(got, want):
+            assert g.shape == w.shape and np.array_equal(g, w)
+        assert np.shares_memory(got[0], bufs[0])
+    with pytest.raises(pkv.PkvError):
+        a.prepare_step([0, 1], maxb + 1, out=bufs)                 # row width differs
+    with pytest.raises(pkv.PkvError):
+        a.prepare_step([0, 1], maxb, out=(bufs[0].astype(np.int64),) + bufs[1:])
+    with pytest.raises(pkv.PkvError):
+        a.prepare_step([0, 1, 2, 3], maxb, max_copies=8, out=bufs)  # copies too small
+    assert [a.info(s) for s in range(4)] == [b.info(s) for s in range(4)]
