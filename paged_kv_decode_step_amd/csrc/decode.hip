@@ -1052,7 +1052,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
   // With several new tokens per request, merge wavefront mw takes the G
   // columns of new token qi = mw % TQ of the sequence whose header
   // wavefront mw / TQ left, so each merges G columns as with one token.
-  const int mw = uniform(blockIdx.x * (kBlockThreads / 64) + (threadIdx.x >> 6));
+  const int mw = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   const int w = TQ > 1 ? mw / TQ : mw;
   const int qi = TQ > 1 ? mw - w * TQ : 0;
   const int4 hdr = p.headers[w];
@@ -1127,11 +1127,15 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
 }
 
 // 16-byte chunks per lane the merge needs for G*D accumulators: a power of
-// two >= G*D / 256.
+// two >= G*D / 256.  One merge wavefront per attention wavefront and new
+// token; with several new tokens the wavefronts go one per workgroup, which
+// dispatches the larger grid faster (4 new tokens, 64 requests: 13.0 -> 10.0
+// us), while with one token four per workgroup is as fast or faster.
 template <bool IO_BF16, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream, hipEvent_t* ev) {
   const int need = (p.group * D / 4 + 63) / 64;
-  const dim3 grid(p.n_waves / 4 * p.n_qtok), block(kBlockThreads);
+  const int threads = p.n_qtok > 1 ? 64 : kBlockThreads;     // n_waves is a multiple of 4
+  const dim3 grid(p.n_waves / (threads / 64) * p.n_qtok), block(threads);
   hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
   if (need <= 1) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 1>), grid, block, 0, stream, e0, e1, 0, p);
   else if (need <= 2) hipExtLaunchKernelGGL((decode_merge_kernel<IO_BF16, D, 2>), grid, block, 0, stream, e0, e1, 0, p);
