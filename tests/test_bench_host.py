@@ -1,0 +1,52 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, and the algorithmic
+byte count of a step against an item-by-item count on small workloads."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def count_bytes(wl, window, new_tokens):
+    """Every byte a step must move, request by request and token by token."""
+    c = wl.cfg
+    kv, io = bench.ELEM[c.kv_dtype], bench.ELEM[c.io_dtype]
+    bs, hkv, hq, d, T = c.block_size, c.n_kv_heads, c.n_q_heads, c.head_dim, new_tokens
+    total = 0
+    for L in (int(x) for x in wl.context_lens):
+        first = max(L - window, 0) if window > 0 else 0
+        for t in range(first, L):
+            total += 2 * hkv * d * kv          # K and V of token t: read, or written when new
+        total += T * hq * d * io * 2           # q read, out written
+        total += T * 2 * hkv * d * io          # k_new, v_new read
+        total += T * 2 * (d // 2) * 4          # cos and sin rows of each new position
+        last = (L - 1) // bs
+        total += 4 * (last - first // bs + 1)  # table entries of the blocks read
+        total += 4 + 4                         # position and length
+    if c.kv_dtype == "fp8":
+        total += 4 * hkv * 4                   # K and V scales and their inverses
+    return total
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("window,new_tokens", [(0, 1), (0, 3), (5, 1), (20, 2), (1000, 1)])
+def test_algorithmic_bytes_counts_every_item(kv, window, new_tokens):
+    lens = [3, 16, 17, 40, 129]
+    io = "f32" if kv == "f32" else "bf16"
+    wl = workloads.custom_workload(lens, n_q_heads=8, n_kv_heads=2, head_dim=64, block_size=16,
+                                   kv_dtype=kv, io_dtype=io, rope_theta=1.0e4, seed=1)
+    assert bench.algorithmic_bytes(wl, window, new_tokens) == count_bytes(wl, window, new_tokens)
