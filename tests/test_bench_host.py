@@ -50,3 +50,14 @@ def test_algorithmic_bytes_counts_every_item(kv, window, new_tokens):
     wl = workloads.custom_workload(lens, n_q_heads=8, n_kv_heads=2, head_dim=64, block_size=16,
                                    kv_dtype=kv, io_dtype=io, rope_theta=1.0e4, seed=1)
     assert bench.algorithmic_bytes(wl, window, new_tokens) == count_bytes(wl, window, new_tokens)
+
+
+def test_traffic_is_reported_only_for_the_kernel_it_was_measured_on(monkeypatch):
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        rec = json.load(fh)
+    name = "llama3_8b_b64_gqa4_d128_bf16"
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec[name]["kernel_hash"])
+    assert bench.measured_traffic(name, 1.0) == rec[name]["bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.measured_traffic(name, 1.0) is None
+    assert bench.measured_traffic("no_such_workload", 1.0) is None
