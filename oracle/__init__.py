@@ -28,7 +28,9 @@ Blackwell").  The readings taken where the pages are silent are listed in the
 docstrings of the functions that take them.
 
 Pins (tests marked ``not gpu``): codecs against all 256 FP8 codes and torch's
-casts; RoPE against closed forms and the relative-position identity;
+casts; the FP8 cache path against the E4M3 rounding bound of the raw values,
+torch's SDPA on K/V dequantised by torch, a brute force and a hand-worked
+step; RoPE against closed forms and the relative-position identity;
 attention against closed forms (one token, identical keys, zero query),
 linearity, block-permutation invariance, a padded static batch computed on a
 separate dense path, ``scaled_dot_product_attention`` in float64 and an
