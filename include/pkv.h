@@ -37,6 +37,15 @@
  * call.  Calls that take a stream refuse (PKV_ERR_INVALID) one that is not on
  * the pool's device; NULL is the current device's default stream.  Calls
  * that allocate do so on the pool's device, whichever device is current.
+ *
+ * HIP graphs.  decode_step and decode_step_multi launch their kernels with
+ * the pool's settings (window, tuning, RoPE table and workspace addresses)
+ * as kernel arguments, and (with timing off and PKV_DEBUG unset) never
+ * allocate, synchronise or memset, so they can be captured.  A captured graph keeps replaying the settings of capture
+ * time: re-capture after kv_pool_set_window, kv_pool_set_tuning or a
+ * kv_pool_set_rope that enlarges the table.  Every buffer such a graph
+ * points to stays allocated until kv_pool_destroy (a larger table or
+ * workspace is a new buffer; the old one is kept).
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -119,7 +128,14 @@ typedef struct pkv_pool_info {
 } pkv_pool_info;
 
 /* Create a pool of num_blocks blocks of block_size token slots for n_kv_heads
- * heads of head_dim dimensions in kv_dtype, on the current HIP device.
+ * heads of head_dim dimensions in kv_dtype, on the current HIP device: the
+ * KV cache kept in fixed-size token blocks that requests reach through
+ * their block tables ("Scaling TensorRT-LLM: Kernel Fusion and Inflight
+ * Batching in Production", section "The Paged KV-Cache: vLLM Borrowed by
+ * TensorRT-LLM"; "TensorRT-LLM Guide: High-Throughput GPU Inference
+ * Engine", section "2. Paged KV Cache & Memory Virtualization").  Block ids
+ * are the caller's to hand out (the scheduler's job, same first page,
+ * "What the Scheduler Actually Does").
  * Supported: head_dim in {64, 128}; block_size in {16, 32, 64};
  * 1 <= n_kv_heads <= 256; 1 <= num_blocks < 2^31 and the pool at most 2^40
  * bytes.
@@ -141,10 +157,16 @@ pkv_status kv_pool_destroy(pkv_pool* pool);
  * Errors: INVALID (theta <= 0, max_position < 1), OOM, HIP. */
 pkv_status kv_pool_set_rope(pkv_pool* pool, double theta, int32_t max_position);
 
-/* Set the FP8 scales (host arrays of n_kv_heads fp32 each, all > 0 and
- * finite): a cached code c of head h means c * k_scale[h] (K) or
- * c * v_scale[h] (V).  New tokens are encoded as E4M3(y * fp32(1/scale)) with
- * round-to-nearest-even and saturation to +-448.  Synchronous.  Only for
+/* Set the FP8 scales of an E4M3 cache with precomputed ("delayed") scale
+ * factors ("TensorRT-LLM Guide: High-Throughput GPU Inference Engine",
+ * section "4. Native FP8 Quantization on NVIDIA Hopper & Blackwell"; here one
+ * fp32 scale per KV head for K and one for V, host arrays of n_kv_heads
+ * values, all > 0 and finite): a cached code c of head h means
+ * c * k_scale[h] (K) or c * v_scale[h] (V).  New tokens are encoded as
+ * E4M3(y * fp32(1/scale)) with round-to-nearest-even and saturation to
+ * +-448; a NaN is stored as the NaN code S.1111.111 with its sign.  The NaN
+ * codes read back as NaN, so a NaN in the cache makes the rows that attend
+ * to it NaN, as with a bf16 or fp32 cache.  Synchronous.  Only for
  * PKV_FP8_E4M3 pools (else INVALID). */
 pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, const float* k_scale,
                                   const float* v_scale);
@@ -152,9 +174,38 @@ pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, const float* k_scale,
 /* Describe the pool (layout, device pointers). */
 pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info);
 
-/* One decode step for `batch` requests (asynchronous on `stream`, a
+/* The pool's storage, for callers that fill or read it in place (zero
+ * copy).  The blocks of the paged cache ("Scaling TensorRT-LLM: Kernel
+ * Fusion and Inflight Batching in Production", section "The Paged
+ * KV-Cache: vLLM Borrowed by TensorRT-LLM") are addressed by three byte
+ * strides: byte_strides[0] per block, [1] per KV head, [2] per 16-token
+ * tile, from k_base (K) and v_base (V), device pointers the pool owns.
+ * Inside a tile of *tile_bytes bytes the elements are not strided: they sit
+ * in the matrix-core operand order given above pkv_pool_info (K as 16-byte
+ * rows of x consecutive dims of one token, V as 16-byte rows of four
+ * consecutive tokens of one dim), which no (slot, dim) stride pair can
+ * express.  Errors: INVALID (null argument). */
+pkv_status kv_pool_layout(const pkv_pool* pool, void** k_base, void** v_base,
+                          int64_t byte_strides[3], int32_t* tile_bytes);
+
+/* The RoPE table the kernels read (built by kv_pool_set_rope; RoPE applied
+ * inside the attention kernel, "Scaling TensorRT-LLM: ...", section "What
+ * Gets Fused"): device arrays of *max_position rows of head_dim/2 fp32
+ * values, cos and sin of p * theta^(-2i/head_dim), owned by the pool.
+ * Errors: INVALID (null argument), STATE (no table yet; the pointers are
+ * then NULL and *max_position 0). */
+pkv_status kv_pool_rope_table(const pkv_pool* pool, const float** cos_dev,
+                              const float** sin_dev, int32_t* max_position);
+
+/* One decode step for `batch` requests: the cache update and the attention
+ * fused in one pass ("TensorRT-LLM" glossary, inferensys.com, paragraph on
+ * the KV cache), RoPE applied inside the attention kernel and its
+ * intermediates kept on chip ("Scaling TensorRT-LLM: Kernel Fusion and
+ * Inflight Batching in Production", section "What Gets Fused"), launched
+ * once per iteration after the scheduler has updated the block tables (same
+ * page, "What the Scheduler Actually Does").  Asynchronous on `stream`, a
  * hipStream_t; NULL = the default stream; no host synchronisation unless the
- * environment variable PKV_DEBUG=1 asks for device-argument validation).
+ * environment variable PKV_DEBUG=1 asks for device-argument validation.
  *
  * Arguments (device pointers, contiguous, row-major; q, k_new, v_new and out
  * 16-byte aligned, the int32 arrays 4-byte aligned):
@@ -286,6 +337,18 @@ pkv_status kv_pool_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_p
 pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable);
 pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms,
                                int32_t* calls);
+
+/* Read `bytes` of device memory at `src` once with the attention kernel's
+ * 16-byte nontemporal loads, on the current device, asynchronously on
+ * `stream` (NULL = the default stream): the bandwidth a plain streaming read
+ * reaches, the reference next to the nominal HBM peak when a step is judged
+ * by its HBM bandwidth (decode waits on memory transfers: "TensorRT-LLM
+ * Guide: High-Throughput GPU Inference Engine", section "The Problem: The
+ * Memory-Bandwidth Wall and Static Batching Inefficiencies").  src: device,
+ * 16-byte aligned; bytes: a positive multiple of 16; sink: device, 1 KiB,
+ * written only in the unlikely case that the folded data equals a fixed
+ * constant.  Errors: INVALID, HIP. */
+pkv_status pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* pkv_last_error(void);

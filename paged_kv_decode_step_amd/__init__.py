@@ -19,7 +19,7 @@ import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
 __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
-    "EXPORTED_SYMBOLS", "BlockAllocator", "decode_step_multi",
+    "EXPORTED_SYMBOLS", "BlockAllocator", "decode_step_multi", "stream_read",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -32,14 +32,15 @@ _STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "OOM", -4: "HIP",
 # every function include/pkv.h declares
 EXPORTED_SYMBOLS = (
     "kv_pool_create", "kv_pool_destroy", "kv_pool_set_rope",
-    "kv_pool_set_fp8_scales", "kv_pool_get_info", "decode_step",
+    "kv_pool_set_fp8_scales", "kv_pool_get_info", "kv_pool_layout",
+    "kv_pool_rope_table", "decode_step",
     "kv_pool_device_errors", "kv_pool_set_tuning", "kv_pool_enable_timing",
     "kv_pool_read_timing", "pkv_last_error",
     "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
     "pkv_tile_tokens", "kv_pool_copy_blocks", "kv_pool_set_window", "decode_step_multi",
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
     "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
-    "pkv_alloc_prepare_step",
+    "pkv_alloc_prepare_step", "pkv_stream_read",
 )
 
 
@@ -87,6 +88,9 @@ def load_library(path: str = LIB_PATH):
         "kv_pool_set_rope": (I32, [P, D, I32]),
         "kv_pool_set_fp8_scales": (I32, [P, FP, FP]),
         "kv_pool_get_info": (I32, [P, ctypes.POINTER(_Info)]),
+        "kv_pool_layout": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P),
+                                 ctypes.POINTER(I64), IP]),
+        "kv_pool_rope_table": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), IP]),
         "decode_step": (I32, [P, P, P, P, I32, P, P, I32, P, I32, I32, P, P]),
         "kv_pool_device_errors": (I32, [P, ctypes.POINTER(ctypes.c_uint32)]),
         "kv_pool_set_tuning": (I32, [P, I32, I32, I32, I32, I32]),
@@ -111,6 +115,7 @@ def load_library(path: str = LIB_PATH):
         "pkv_seq_release": (I32, [P, I32]),
         "pkv_seq_info": (I32, [P, I32, IP, IP, IP, I32]),
         "pkv_alloc_prepare_step": (I32, [P, IP, I32, I32, IP, IP, IP, IP, I32, IP]),
+        "pkv_stream_read": (I32, [P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +215,29 @@ class KVPool:
         inf = _Info()
         _check(_lib.kv_pool_get_info(self.handle, ctypes.byref(inf)))
         return {k: getattr(inf, k) for k, _ in _Info._fields_}
+
+    def layout(self) -> dict:
+        """``kv_pool_layout``: K and V base addresses, the byte strides per
+        block, KV head and 16-token tile, and the tile's size in bytes."""
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        st = (ctypes.c_int64 * 3)()
+        tb = ctypes.c_int32()
+        _check(_lib.kv_pool_layout(self.handle, ctypes.byref(k), ctypes.byref(v), st,
+                                   ctypes.byref(tb)))
+        return {"k_base": k.value, "v_base": v.value, "byte_strides": tuple(st),
+                "tile_bytes": tb.value}
+
+    def rope_table(self):
+        """``kv_pool_rope_table``: the device tables as float32 tensors
+        ``[max_position, head_dim / 2]`` (cos, sin), zero copy."""
+        c, s = ctypes.c_void_p(), ctypes.c_void_p()
+        n = ctypes.c_int32()
+        _check(_lib.kv_pool_rope_table(self.handle, ctypes.byref(c), ctypes.byref(s),
+                                       ctypes.byref(n)))
+        shape = (n.value, self.head_dim // 2)
+        dev = f"cuda:{self.device}"
+        return (torch.as_tensor(_CudaArray(c.value, shape, "<f4"), device=dev),
+                torch.as_tensor(_CudaArray(s.value, shape, "<f4"), device=dev))
 
     def device_errors(self) -> int:
         f = ctypes.c_uint32()
@@ -440,6 +468,24 @@ def decode_step_multi(pool: KVPool, q, k_new, v_new, positions, block_tables,
                                  _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
                                  _ptr(context_lens), batch, hq, _ptr(out),
                                  ctypes.c_void_p(stream)))
+
+
+def stream_read(src, sink, stream=None) -> None:
+    """``pkv_stream_read``: read all of the contiguous device tensor ``src``
+    once with 16-byte nontemporal loads (asynchronous; the achievable-peak
+    reference of the benchmark).  ``sink``: a device tensor of >= 1 KiB."""
+    lib = load_library()
+    if not src.is_contiguous() or src.device.type != "cuda" or sink.device != src.device:
+        raise PkvError(-1, "src and sink must be contiguous tensors on one GPU")
+    if sink.numel() * sink.element_size() < 1024:
+        raise PkvError(-1, "sink must hold at least 1 KiB")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device).cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        _check(lib.pkv_stream_read(_ptr(src), int(nbytes), _ptr(sink), ctypes.c_void_p(stream)))
 
 
 # ---- host-only helpers -----------------------------------------------------

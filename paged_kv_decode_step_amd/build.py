@@ -15,6 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = [os.path.join(HERE, "csrc", "decode.hip"),
            os.path.join(HERE, "csrc", "blocks.hip"),
+           os.path.join(HERE, "csrc", "stream_read.hip"),
            os.path.join(HERE, "csrc", "pkv_host.cpp"),
            os.path.join(HERE, "csrc", "block_alloc.cpp")]
 

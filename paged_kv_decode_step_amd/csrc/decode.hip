@@ -166,18 +166,14 @@ __device__ __forceinline__ uint32_t fp8_encode(float v) {
   return sign | ((uint32_t)(e + 7) << 3) | m;
 }
 
-// Two E4M3 codes spread as bytes [0, c0, 0, c1] -> two f16 holding
-// value * 2^-8, exactly (subnormals included): the exponent and mantissa
-// bits shift into place and the bias difference is the factor.
-__device__ __forceinline__ uint32_t fp8x2_spread_to_f16x2(uint32_t s) {
-  return ((s >> 1) & 0x3f803f80u) | (s & 0x80008000u);
-}
-
-// Four E4M3 codes (bytes of w, lowest first) -> four f16 (value * 2^-8).
+// Four E4M3 codes (bytes of w, lowest first) -> four f16 holding the same
+// values: gfx950's OCP FP8 conversion, two codes per instruction, with a
+// scale of 1.  Every E4M3 value (subnormals included) is an f16 value, so
+// the conversion is exact, and the NaN codes S.1111.111 give NaN.
 __device__ __forceinline__ f16x4_t fp8x4_to_f16x4(uint32_t w) {
   u32x2_t r;
-  r[0] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x010c000cu));
-  r[1] = fp8x2_spread_to_f16x2(__builtin_amdgcn_perm(0u, w, 0x030c020cu));
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
   return __builtin_bit_cast(f16x4_t, r);
 }
 
@@ -642,10 +638,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       }
     } else if constexpr (KV == KV_FP8) {
       // The query is scaled by a power of two so that it fits f16 with room
-      // to spare; the factor goes back into the score scale, with the K scale
-      // and the 2^-8 of the code conversion.  A rotation keeps each pair's
-      // norm, so |rotated| <= sqrt(2) * max |raw| bounds the scale from the
-      // raw row before anything is rotated.
+      // to spare; the factor goes back into the score scale, with the K
+      // scale.  A rotation keeps each pair's norm, so
+      // |rotated| <= sqrt(2) * max |raw| bounds the scale from the raw row
+      // before anything is rotated.
       float amax = 0.f;
       {
         const int d0 = C::X * lq;
@@ -664,8 +660,8 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
         ex = ex > 15 ? ex - 15 : 0;
       }
       const float qs = __builtin_ldexpf(1.0f, -ex);
-      sscale = p.sm_scale_log2 * p.fp8_scales[h] * __builtin_ldexpf(1.0f, 8 + ex);
-      vsc = 256.0f * p.fp8_scales[hkv + h];
+      sscale = p.sm_scale_log2 * p.fp8_scales[h] * __builtin_ldexpf(1.0f, ex);
+      vsc = p.fp8_scales[hkv + h];
 #pragma unroll
       for (int c = 0; c < NPAIR; ++c) {
         float y0[C::X], y1[C::X];
@@ -701,13 +697,19 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     // the pool and to LDS; the tile registers get them at the last tile, so
     // it does not matter whether that tile's loads left before or after
     // these stores.
+    // An out-of-range block id for the new token's slot raises the flag and
+    // skips the append: nothing is written to another block, and the
+    // request's output is garbage (its last tile was read from block 0).
+    int blk = 0;
     if (app) {
-      r0 = (L - 1) & 15;
-      int blk = tables[(int64_t)b * p.max_blocks + (L - 1) / BS];
+      blk = tables[(int64_t)b * p.max_blocks + (L - 1) / BS];
       if ((unsigned)blk >= (unsigned)p.num_blocks) {
         bad_block |= 1u;
-        blk = 0;
+        app = false;
       }
+    }
+    if (app) {
+      r0 = (L - 1) & 15;
       const int64_t nrow = ((int64_t)b * hkv + h) * D;
       float inv_k = 1.0f, inv_v = 1.0f;
       if constexpr (KV == KV_FP8) {
@@ -850,20 +852,21 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     const float mb = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = exp2_fast(m_run - mb);
     m_run = m_new;
-    float ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = exp2_fast(s[r] - mb);
-      ps += s[r];
-    }
-    l_run = __builtin_fmaf(l_run, alpha, ps);
+    for (int r = 0; r < 4; ++r) s[r] = exp2_fast(s[r] - mb);
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) acc[nt] *= alpha;
 
+    // The normaliser sums the probabilities as the P V product sees them
+    // (rounded to bf16 or f16 for the matrix cores), so that the output's
+    // weights sum to one exactly.
     if constexpr (KV == KV_BF16) {
       u32x2_t pw2;
       pw2[0] = pack_bf16x2(s[0], s[1]);
       pw2[1] = pack_bf16x2(s[2], s[3]);
+      const float ps = (__uint_as_float(pw2[0] << 16) + __uint_as_float(pw2[0] & 0xffff0000u)) +
+                       (__uint_as_float(pw2[1] << 16) + __uint_as_float(pw2[1] & 0xffff0000u));
+      l_run = __builtin_fmaf(l_run, alpha, ps);
       const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw2);
 #pragma unroll
       for (int c = 0; c < C::KCH; ++c)
@@ -880,6 +883,8 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       pw2[0] = pack_f16x2(s[0], s[1]);
       pw2[1] = pack_f16x2(s[2], s[3]);
       const f16x4_t ph = __builtin_bit_cast(f16x4_t, pw2);
+      const float ps = ((float)ph[0] + (float)ph[1]) + ((float)ph[2] + (float)ph[3]);
+      l_run = __builtin_fmaf(l_run, alpha, ps);
 #pragma unroll
       for (int c = 0; c < C::KCH; ++c)
 #pragma unroll
@@ -887,6 +892,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
           acc[4 * c + k] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16x4(t.v[c][k]), ph,
                                                                  acc[4 * c + k], 0, 0, 0);
     } else {
+      l_run = __builtin_fmaf(l_run, alpha, (s[0] + s[1]) + (s[2] + s[3]));
 #pragma unroll
       for (int c = 0; c < C::KCH; ++c) {
         const f32x4_t vf = __builtin_bit_cast(f32x4_t, t.v[c]);

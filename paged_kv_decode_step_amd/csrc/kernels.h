@@ -75,6 +75,12 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int32_t n, int64_t block_byt
                               int32_t num_blocks, void* k_pool, void* v_pool, uint32_t* err,
                               hipStream_t stream);
 
+// Read `bytes` (a multiple of 16) at `src` with n_groups workgroups of
+// nontemporal 16-byte loads; sink (256 words) is written only if the folded
+// data equals a fixed constant.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int n_groups,
+                              hipStream_t stream);
+
 // Bytes of workspace the kernels need for n_waves wavefronts (partials).
 inline size_t partials_bytes(int n_waves, int head_dim) {
   return (size_t)n_waves * 2 * partial_floats(head_dim) * sizeof(float);

@@ -98,6 +98,7 @@ struct pkv_pool {
   int64_t kv_bytes = 0;
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
+  size_t rope_cap = 0;             // floats each table buffer holds
   int32_t rope_max_pos = 0;
   double rope_theta = 0.0;
   float* fp8_scales = nullptr;     // [4][Hkv]
@@ -111,12 +112,17 @@ struct pkv_pool {
   int occ_blocks = 0;              // resident workgroups per CU (occupancy)
   int waves_per_cu = 0;
   int n_waves = 0;
+  int ws_waves = 0;                // wavefronts the workspace has room for
   int min_units = 16;
   int piece_cost = 0;       // resolved (never the automatic -1)
   int ring_tiles = 0;
   int young_pct = 100;      // share weight of later workgroups, % of the first's
   int odd_pct = 100;        // share weight of odd workgroups, % of the even ones'
   int window = 0;           // attention window in tokens (0 = the whole context)
+  // Buffers replaced by a larger one (RoPE table, workspace).  A graph
+  // captured before the replacement still points at them, so they are freed
+  // only with the pool.
+  std::vector<void*> retired;
   // measurement: per call, start and stop events of each of the two kernels
   bool timing = false;
   std::vector<hipEvent_t> events;
@@ -142,6 +148,7 @@ struct DeviceGuard {
 static void free_pool(pkv_pool* p) {
   if (!p) return;
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  for (void* r : p->retired) (void)hipFree(r);
   (void)hipFree(p->k);
   (void)hipFree(p->v);
   (void)hipFree(p->rope_cos);
@@ -159,17 +166,27 @@ static pkv_status size_workspace(pkv_pool* p, int waves_per_cu) {
   wpc = std::max(4, std::min(wpc, 32));
   wpc = (wpc + 3) / 4 * 4;
   const int n_waves = p->cus * wpc;
-  if (n_waves == p->n_waves && p->partials) return PKV_OK;
-  (void)hipFree(p->partials);
-  (void)hipFree(p->headers);
-  p->partials = nullptr;
-  p->headers = nullptr;
-  p->n_waves = 0;
+  if (p->partials && n_waves <= p->ws_waves) {     // the workspace holds them
+    p->n_waves = n_waves;
+    p->waves_per_cu = wpc;
+    return PKV_OK;
+  }
+  // a larger workspace; the old one is kept until the pool is destroyed
   const size_t pb = pkv::partials_bytes(n_waves, p->head_dim);
-  hipError_t e = hipMalloc(&p->partials, pb);
+  float* partials = nullptr;
+  int4* headers = nullptr;
+  hipError_t e = hipMalloc(&partials, pb);
   if (e != hipSuccess) return fail(PKV_ERR_OOM, "workspace (%zu bytes): %s", pb, hipGetErrorString(e));
-  e = hipMalloc(&p->headers, sizeof(int4) * n_waves);
-  if (e != hipSuccess) return fail(PKV_ERR_OOM, "headers: %s", hipGetErrorString(e));
+  e = hipMalloc(&headers, sizeof(int4) * n_waves);
+  if (e != hipSuccess) {
+    (void)hipFree(partials);
+    return fail(PKV_ERR_OOM, "headers: %s", hipGetErrorString(e));
+  }
+  if (p->partials) p->retired.push_back(p->partials);
+  if (p->headers) p->retired.push_back(p->headers);
+  p->partials = partials;
+  p->headers = headers;
+  p->ws_waves = n_waves;
   p->n_waves = n_waves;
   p->waves_per_cu = wpc;
   p->ws_bytes = (int64_t)pb + (int64_t)sizeof(int4) * n_waves + (int64_t)pkv::kDummyBytes;
@@ -276,14 +293,29 @@ pkv_status kv_pool_set_rope(pkv_pool* pool, double theta, int32_t max_position) 
   pkv_status st = pkv_rope_table_host(theta, pool->head_dim, max_position, c.data(), s.data());
   if (st != PKV_OK) return st;
   DeviceGuard g(pool->device);
-  (void)hipFree(pool->rope_cos);
-  (void)hipFree(pool->rope_sin);
-  pool->rope_cos = pool->rope_sin = nullptr;
+  hipError_t e;
+  if (n > pool->rope_cap) {
+    // a larger table: new buffers, the old ones kept until the pool is
+    // destroyed (a graph captured earlier still reads them)
+    float *cs = nullptr, *sn = nullptr;
+    e = hipMalloc(&cs, n * sizeof(float));
+    if (e != hipSuccess) return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+    e = hipMalloc(&sn, n * sizeof(float));
+    if (e != hipSuccess) {
+      (void)hipFree(cs);
+      return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+    }
+    if (pool->rope_cos) pool->retired.push_back(pool->rope_cos);
+    if (pool->rope_sin) pool->retired.push_back(pool->rope_sin);
+    pool->rope_cos = cs;
+    pool->rope_sin = sn;
+    pool->rope_cap = n;
+  } else {
+    // rewritten in place: wait for any step that may still read the table
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  }
   pool->rope_max_pos = 0;
-  hipError_t e = hipMalloc(&pool->rope_cos, n * sizeof(float));
-  if (e != hipSuccess) return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
-  e = hipMalloc(&pool->rope_sin, n * sizeof(float));
-  if (e != hipSuccess) return fail(PKV_ERR_OOM, "rope table: %s", hipGetErrorString(e));
   e = hipMemcpy(pool->rope_cos, c.data(), n * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy rope");
   e = hipMemcpy(pool->rope_sin, s.data(), n * sizeof(float), hipMemcpyHostToDevice);
@@ -344,6 +376,32 @@ pkv_status kv_pool_get_info(const pkv_pool* pool, pkv_pool_info* info) {
   info->odd_weight_pct = pool->odd_pct;
   info->window = pool->window;
   info->n_first = std::min(pool->n_waves, 4 * pool->cus);
+  return PKV_OK;
+}
+
+pkv_status kv_pool_layout(const pkv_pool* pool, void** k_base, void** v_base,
+                          int64_t byte_strides[3], int32_t* tile_bytes) {
+  if (!pool || !k_base || !v_base || !byte_strides || !tile_bytes)
+    return fail(PKV_ERR_INVALID, "null argument");
+  const int64_t t = (int64_t)pkv::kTileTokens * pool->head_dim * elem_bytes(pool->kv_dtype);
+  const int64_t tpb = pool->block_size / pkv::kTileTokens;
+  *k_base = pool->k;
+  *v_base = pool->v;
+  byte_strides[0] = (int64_t)pool->n_kv_heads * tpb * t;   // block
+  byte_strides[1] = tpb * t;                               // KV head
+  byte_strides[2] = t;                                     // 16-token tile
+  *tile_bytes = (int32_t)t;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_rope_table(const pkv_pool* pool, const float** cos_dev, const float** sin_dev,
+                              int32_t* max_position) {
+  if (!pool || !cos_dev || !sin_dev || !max_position)
+    return fail(PKV_ERR_INVALID, "null argument");
+  *cos_dev = pool->rope_cos;
+  *sin_dev = pool->rope_sin;
+  *max_position = pool->rope_max_pos;
+  if (pool->rope_max_pos < 1) return fail(PKV_ERR_STATE, "kv_pool_set_rope was not called");
   return PKV_OK;
 }
 
@@ -620,6 +678,22 @@ pkv_status kv_pool_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_p
                                                (int32_t)pool->num_blocks, pool->k, pool->v,
                                                pool->err, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "block copy launch");
+  return PKV_OK;
+}
+
+pkv_status pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(PKV_ERR_INVALID, "null pointer");
+  if (bytes <= 0 || bytes % 16) return fail(PKV_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if ((uintptr_t)src % 16 || (uintptr_t)sink % 4)
+    return fail(PKV_ERR_INVALID, "src must be 16-byte aligned, sink 4-byte aligned");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  // 16 workgroups of 256 threads per compute unit, as many as fit at once
+  e = pkv::launch_stream_read(src, bytes, sink, 16 * std::max(cus, 1),
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
   return PKV_OK;
 }
 

@@ -251,3 +251,30 @@ def test_partition_with_a_window_reads_only_the_window(window):
             L = lens[b]
             lo = (L - window) // 16 if L > window else 0
             assert n == -(-L // 16) - lo       # the tiles holding tokens [L - window, L)
+
+
+def test_layout_and_rope_table_calls_check_their_arguments():
+    """kv_pool_layout and kv_pool_rope_table through ctypes: a null pool or
+    output pointer is refused with INVALID before anything is read."""
+    import ctypes
+    lib = pkv.load_library()
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    st = (ctypes.c_int64 * 3)()
+    tb = ctypes.c_int32()
+    assert lib.kv_pool_layout(None, ctypes.byref(k), ctypes.byref(v), st, ctypes.byref(tb)) == INVALID
+    assert "null" in pkv.last_error()
+    c, s = ctypes.c_void_p(), ctypes.c_void_p()
+    n = ctypes.c_int32()
+    assert lib.kv_pool_rope_table(None, ctypes.byref(c), ctypes.byref(s), ctypes.byref(n)) == INVALID
+    assert "null" in pkv.last_error()
+
+
+def test_stream_read_checks_its_arguments():
+    """pkv_stream_read refuses a null pointer or a size that is not a positive
+    multiple of 16 before touching the GPU."""
+    import ctypes
+    lib = pkv.load_library()
+    assert lib.pkv_stream_read(None, 1024, ctypes.c_void_p(0x1000), None) == INVALID
+    assert lib.pkv_stream_read(ctypes.c_void_p(0x1000), 1000, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pkv_stream_read(ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x2000), None) == INVALID
+    assert lib.pkv_stream_read(ctypes.c_void_p(0x1008), 1024, ctypes.c_void_p(0x2000), None) == INVALID
