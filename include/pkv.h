@@ -245,6 +245,27 @@ pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new,
                        int32_t batch, int32_t n_q_heads, void* out,
                        void* stream);
 
+/* decode_step for callers that cannot allocate device memory at step time:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels, arguments and results as decode_step, with
+ * the split-K workspace (partial softmax states and per-wavefront headers)
+ * in a fixed per-device array that the library holds from the moment its
+ * code object loads until the process ends, instead of the pool's: 32.5 MiB
+ * per GPU, room for 2048 wavefronts at head_dim <= 128.  It allocates
+ * nothing, synchronises nothing, and neither reads PKV_DEBUG nor records
+ * timing events.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from different pools) race
+ * and give wrong outputs, so serialise them.  The array keeps the last
+ * call's partial states; none of it needs clearing, since every launch
+ * writes all of it that it later reads.  Errors as decode_step, plus
+ * UNSUPPORTED when the pool runs more than 2048 wavefronts
+ * (kv_pool_set_tuning above 8 per compute unit on 256 compute units). */
+pkv_status decode_step_noalloc(pkv_pool* pool, const void* q, const void* k_new,
+                               const void* v_new, pkv_dtype io_dtype,
+                               const int32_t* positions, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t batch, int32_t n_q_heads, void* out, void* stream);
+
 /* A step that brings n_new >= 1 new tokens per request: a chunk of a long
  * prompt processed beside decoding requests ("Lesson 13.17 TensorRT-LLM:
  * NVIDIA's Optimized Inference Engine", section "The paged KV cache, in-flight

@@ -20,6 +20,7 @@ __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
     "EXPORTED_SYMBOLS", "BlockAllocator", "decode_step_multi", "stream_read",
+    "decode_step_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -40,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "pkv_tile_tokens", "kv_pool_copy_blocks", "kv_pool_set_window", "decode_step_multi",
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
     "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
-    "pkv_alloc_prepare_step", "pkv_stream_read",
+    "pkv_alloc_prepare_step", "pkv_stream_read", "decode_step_noalloc",
 )
 
 
@@ -92,6 +93,7 @@ def load_library(path: str = LIB_PATH):
                                  ctypes.POINTER(I64), IP]),
         "kv_pool_rope_table": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), IP]),
         "decode_step": (I32, [P, P, P, P, I32, P, P, I32, P, I32, I32, P, P]),
+        "decode_step_noalloc": (I32, [P, P, P, P, I32, P, P, I32, P, I32, I32, P, P]),
         "kv_pool_device_errors": (I32, [P, ctypes.POINTER(ctypes.c_uint32)]),
         "kv_pool_set_tuning": (I32, [P, I32, I32, I32, I32, I32]),
         "kv_pool_enable_timing": (I32, [P, I32]),
@@ -275,16 +277,9 @@ class KVPool:
             pass
 
 
-def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
-                context_lens, out, stream=None) -> None:
-    """Launch one decode step (asynchronous on ``stream``; torch tensors).
-
-    ``q``/``out`` ``[B, Hq, D]``, ``k_new``/``v_new`` ``[B, Hkv, D]`` in the
-    I/O dtype (float32 or bfloat16), ``positions``/``context_lens`` int32
-    ``[B]``, ``block_tables`` int32 ``[B, max_blocks]``, all contiguous on the
-    pool's device.
-    """
-    lib = load_library()
+def _step_args(pool: KVPool, q, k_new, v_new, positions, block_tables, context_lens, out,
+               stream):
+    """Checked C arguments of ``decode_step`` and ``decode_step_noalloc``."""
     io = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(q.dtype)
     if io is None:
         raise PkvError(-1, f"unsupported io dtype {q.dtype}")
@@ -316,10 +311,33 @@ def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
-    _check(lib.decode_step(pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), DTYPES[io],
-                           _ptr(positions), _ptr(block_tables), int(block_tables.shape[1]),
-                           _ptr(context_lens), batch, hq, _ptr(out),
-                           ctypes.c_void_p(stream)))
+    return (pool.handle, _ptr(q), _ptr(k_new), _ptr(v_new), DTYPES[io], _ptr(positions),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), batch, hq,
+            _ptr(out), ctypes.c_void_p(stream))
+
+
+def decode_step(pool: KVPool, q, k_new, v_new, positions, block_tables,
+                context_lens, out, stream=None) -> None:
+    """Launch one decode step (asynchronous on ``stream``; torch tensors).
+
+    ``q``/``out`` ``[B, Hq, D]``, ``k_new``/``v_new`` ``[B, Hkv, D]`` in the
+    I/O dtype (float32 or bfloat16), ``positions``/``context_lens`` int32
+    ``[B]``, ``block_tables`` int32 ``[B, max_blocks]``, all contiguous on the
+    pool's device.
+    """
+    lib = load_library()
+    _check(lib.decode_step(*_step_args(pool, q, k_new, v_new, positions, block_tables,
+                                       context_lens, out, stream)))
+
+
+def decode_step_noalloc(pool: KVPool, q, k_new, v_new, positions, block_tables,
+                        context_lens, out, stream=None) -> None:
+    """``decode_step`` with the split-K workspace in the library's fixed
+    per-device array instead of the pool's (``decode_step_noalloc``): nothing
+    is allocated; calls that overlap on one GPU race."""
+    lib = load_library()
+    _check(lib.decode_step_noalloc(*_step_args(pool, q, k_new, v_new, positions, block_tables,
+                                               context_lens, out, stream)))
 
 
 class BlockAllocator:

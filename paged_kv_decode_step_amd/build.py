@@ -16,6 +16,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = [os.path.join(HERE, "csrc", "decode.hip"),
            os.path.join(HERE, "csrc", "blocks.hip"),
            os.path.join(HERE, "csrc", "stream_read.hip"),
+           os.path.join(HERE, "csrc", "noalloc.hip"),
            os.path.join(HERE, "csrc", "pkv_host.cpp"),
            os.path.join(HERE, "csrc", "block_alloc.cpp")]
 

@@ -82,9 +82,29 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
                               hipStream_t stream);
 
 // Bytes of workspace the kernels need for n_waves wavefronts (partials).
-inline size_t partials_bytes(int n_waves, int head_dim) {
+constexpr size_t partials_bytes(int n_waves, int head_dim) {
   return (size_t)n_waves * 2 * partial_floats(head_dim) * sizeof(float);
 }
+
+// Bytes of a whole split-K workspace: the partial states, then (at the next
+// 256-byte boundary) one header per wavefront.
+constexpr size_t headers_offset(int n_waves, int head_dim) {
+  return (partials_bytes(n_waves, head_dim) + 255) / 256 * 256;
+}
+constexpr size_t workspace_bytes(int n_waves, int head_dim) {
+  return headers_offset(n_waves, head_dim) + (size_t)n_waves * 16;
+}
+
+// The fixed per-device workspace of decode_step_noalloc: room for 2048
+// wavefronts (8 per compute unit on 256 compute units) at head_dim <= 128,
+// about 32.5 MiB.
+constexpr int kScratchMaxWaves = 2048;
+constexpr int kScratchMaxHeadDim = 128;
+constexpr size_t kScratchBytes = workspace_bytes(kScratchMaxWaves, kScratchMaxHeadDim);
+
+// Device address of the fixed workspace on `device` (looked up once per
+// device, with that device current, then kept).
+hipError_t scratch_address(int device, void** addr);
 
 constexpr size_t kDummyBytes = 16384;
 

@@ -544,11 +544,18 @@ static pkv_status check_stream_device(const pkv_pool* pool, hipStream_t st) {
   return PKV_OK;
 }
 
+// A split-K workspace: the pool's own, or the fixed per-device one.
+struct Workspace {
+  float* partials;
+  int4* headers;
+};
+
 static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
                               const void* v_new, pkv_dtype io_dtype, int32_t n_new,
                               const int32_t* positions, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
-                              int32_t batch, int32_t n_q_heads, void* out, void* stream);
+                              int32_t batch, int32_t n_q_heads, void* out, void* stream,
+                              const Workspace* fixed = nullptr);
 
 pkv_status decode_step(pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
                        pkv_dtype io_dtype, const int32_t* positions, const int32_t* block_tables,
@@ -582,11 +589,36 @@ pkv_status decode_step_multi(pkv_pool* pool, const void* q, const void* k_new, c
                      max_blocks_per_seq, context_lens, batch, n_q_heads, out, stream);
 }
 
+pkv_status decode_step_noalloc(pkv_pool* pool, const void* q, const void* k_new,
+                               const void* v_new, pkv_dtype io_dtype, const int32_t* positions,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t batch, int32_t n_q_heads,
+                               void* out, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
+  if (pool->n_waves > pkv::kScratchMaxWaves)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "decode_step_noalloc: the pool runs %d wavefronts, the fixed workspace holds %d",
+                pool->n_waves, pkv::kScratchMaxWaves);
+  if (pool->head_dim > pkv::kScratchMaxHeadDim)
+    return fail(PKV_ERR_UNSUPPORTED, "decode_step_noalloc: head_dim above %d",
+                pkv::kScratchMaxHeadDim);
+  void* base = nullptr;
+  const hipError_t e = pkv::scratch_address(pool->device, &base);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (fixed workspace)");
+  Workspace ws;
+  ws.partials = static_cast<float*>(base);
+  ws.headers = reinterpret_cast<int4*>(static_cast<char*>(base) +
+                                       pkv::headers_offset(pool->n_waves, pool->head_dim));
+  return launch_step(pool, q, k_new, v_new, io_dtype, 1, positions, block_tables,
+                     max_blocks_per_seq, context_lens, batch, n_q_heads, out, stream, &ws);
+}
+
 static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
                               const void* v_new, pkv_dtype io_dtype, int32_t n_new,
                               const int32_t* positions, const int32_t* block_tables,
                               int32_t max_blocks_per_seq, const int32_t* context_lens,
-                              int32_t batch, int32_t n_q_heads, void* out, void* stream) {
+                              int32_t batch, int32_t n_q_heads, void* out, void* stream,
+                              const Workspace* fixed) {
   if (!pool) return fail(PKV_ERR_INVALID, "pool is null");
   pkv_status s = pkv_check_decode_args(pool->num_blocks, pool->block_size, pool->n_kv_heads,
                                        pool->head_dim, pool->kv_dtype, io_dtype, q, k_new, v_new,
@@ -600,7 +632,7 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   hipStream_t st = static_cast<hipStream_t>(stream);
   s = check_stream_device(pool, st);
   if (s != PKV_OK) return s;
-  if (env_int("PKV_DEBUG", 0) == 1) {
+  if (!fixed && env_int("PKV_DEBUG", 0) == 1) {
     s = debug_validate(pool, positions, block_tables, max_blocks_per_seq, context_lens, batch,
                        n_new, st);
     if (s != PKV_OK) return s;
@@ -618,8 +650,8 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   p.rope_cos = pool->rope_cos;
   p.rope_sin = pool->rope_sin;
   p.fp8_scales = pool->fp8_scales;
-  p.partials = pool->partials;
-  p.headers = pool->headers;
+  p.partials = fixed ? fixed->partials : pool->partials;
+  p.headers = fixed ? fixed->headers : pool->headers;
   p.dummy = pool->dummy;
   p.err = pool->err;
   p.num_blocks = (int32_t)pool->num_blocks;
@@ -641,7 +673,7 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   p.window = pool->window;
   p.n_qtok = n_new;
   hipEvent_t* ev = nullptr;
-  if (pool->timing && pool->timed_calls < kMaxTimedCalls) {
+  if (!fixed && pool->timing && pool->timed_calls < kMaxTimedCalls) {
     const size_t need = 4 * (size_t)(pool->timed_calls + 1);
     DeviceGuard g(pool->device);
     while (pool->events.size() < need) {
