@@ -1,10 +1,13 @@
 """Build ``libpkv.so`` (HIP kernels + C ABI) in-tree for gfx950.
 
 Usage: ``python -m paged_kv_decode_step_amd.build`` (or ``build()``).  The
-library lands next to this file, where the binding loads it from.
+library lands next to this file, where the binding loads it from.  The
+sources compile to objects in parallel (the attention kernels once per cache
+type), which are then linked.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -12,13 +15,22 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = [os.path.join(HERE, "csrc", "decode.hip"),
-           os.path.join(HERE, "csrc", "blocks.hip"),
-           os.path.join(HERE, "csrc", "stream_read.hip"),
-           os.path.join(HERE, "csrc", "noalloc.hip"),
-           os.path.join(HERE, "csrc", "pkv_host.cpp"),
-           os.path.join(HERE, "csrc", "block_alloc.cpp")]
+OBJ_DIR = os.path.join(HERE, "_build")
+DECODE = os.path.join(CSRC, "decode.hip")
+KV_KINDS = (0, 1, 2)            # KV_F32, KV_BF16, KV_FP8: one object each
+OTHER_SOURCES = ["blocks.hip", "stream_read.hip", "noalloc.hip", "dispatch.cpp", "pkv_host.cpp",
+                 "host_api.cpp", "block_alloc.cpp"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # the appended key's RoPE is specified as separate fp32 multiplies and
+    # adds; nothing may be contracted into an FMA unless written so
+    "-ffp-contract=off",
+    # packed fp32 VALU ops are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
 
 
 def hipcc() -> str:
@@ -28,30 +40,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def command(out: str = LIB) -> list:
-    return [
-        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # the appended key's RoPE is specified as separate fp32 multiplies
-        # and adds; nothing may be contracted into an FMA unless written so
-        "-ffp-contract=off",
-        # packed fp32 VALU ops are kept out of the generated code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"),
-        *SOURCES, "-o", out,
-    ]
+def compile_jobs(decode_src: str = DECODE, obj_dir: str = OBJ_DIR) -> list:
+    """(command, object) pairs: decode.hip once per cache type, then the rest."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    jobs = []
+    for kv in KV_KINDS:
+        obj = os.path.join(obj_dir, f"decode_kv{kv}.o")
+        jobs.append(([hipcc(), *FLAGS, *inc, f"-DPKV_KV={kv}", "-c", decode_src, "-o", obj], obj))
+    for src in OTHER_SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        jobs.append(([hipcc(), *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    return jobs
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def build(verbose: bool = False, decode_src: str = DECODE, out: str = LIB,
+          obj_dir: str = OBJ_DIR) -> str:
+    """Compile every source (in parallel) and link the shared library."""
+    os.makedirs(obj_dir, exist_ok=True)
+    jobs = compile_jobs(decode_src, obj_dir)
+
+    def run(cmd):
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        results = list(ex.map(run, [cmd for cmd, _ in jobs]))
+    for (cmd, _), res in zip(jobs, results):
+        if res.returncode != 0:
+            sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed building libpkv.so")
+        if verbose:
+            sys.stderr.write(res.stderr)
+    tmp = out + ".tmp"
+    res = run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC",
+               *[obj for _, obj in jobs], "-o", tmp])
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libpkv.so")
-    if verbose:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("linking libpkv.so failed")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

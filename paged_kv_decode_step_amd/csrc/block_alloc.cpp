@@ -29,9 +29,7 @@
 
 #include "../../include/pkv.h"
 
-namespace pkv {
-pkv_status set_error(pkv_status s, const char* msg);   // pkv_host.cpp
-}
+#include "host_errors.h"
 
 namespace {
 

@@ -59,6 +59,12 @@
 #include "kernels.h"
 #include "plan.h"
 
+// One object per cache type: the build compiles this file once for each of
+// KV_F32, KV_BF16 and KV_FP8 (-DPKV_KV=0, 1, 2), in parallel.
+#ifndef PKV_KV
+#error "decode.hip is compiled once per cache type, with -DPKV_KV=<KvKind>"
+#endif
+
 // K+V bytes each wavefront keeps in flight (fp8 needs registers for the code
 // conversions, so it keeps a little less).
 #ifndef PKV_RING_BYTES
@@ -118,6 +124,12 @@ __device__ __forceinline__ float sum_over_lq(float v) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The value of lane (lr + 8) mod 16 of the same row of 16 lanes (DPP
+// row_ror:8): pairs the MFMA columns g and g + 8.
+__device__ __forceinline__ float swap_half_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
 
 // Wait for every vector memory operation of the wavefront (vmcnt 0; the
 // other counters untouched).  Ends a rarely taken branch that stores inside
@@ -331,7 +343,9 @@ __device__ __forceinline__ void walk_next(Walk& w, const int* sP, const int* sLo
 // MQ: every request brings n_qtok > 1 new tokens (appended beforehand by
 // decode_append_kernel); MFMA column lr = qi * G + g holds query head g of new
 // token qi, which attends causally to the tokens [0, L - n_qtok + qi].
-template <int KV, int D, int BS, bool MQ>
+// LO: a bf16 cache, one new token, G <= 8: the MFMA columns g + 8 carry the
+// bf16 low parts of column g's query and probabilities (see lo_cols).
+template <int KV, int D, int BS, bool MQ, bool LO>
 __global__ __launch_bounds__(kBlockThreads)
 __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU, PKV_WAVES_PER_EU)))
 void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
@@ -363,7 +377,20 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int B = p.batch, hkv = p.n_kv_heads, G = p.group;
   const int TQ = MQ ? p.n_qtok : 1;           // new tokens per request
   const int NC = G * TQ;                      // MFMA columns in use (<= 16)
-  const int lane_qi = MQ ? (lr < NC ? lr : 0) / G : 0;   // new token of this lane's column
+  // Low parts.  With a bf16 cache the rotated query and the probabilities
+  // enter the matrix cores rounded to bf16, which costs as much accuracy as
+  // the final rounding of the output.  When the used columns fit in the
+  // first half (NC <= 8), column g + 8 carries the bf16 remainders
+  // x - bf16(x) of column g: the score MFMA then gives both lanes of a pair
+  // the two halves of the score, one row rotation adds them, both lanes run
+  // the same softmax, and the P V MFMA accumulates the high parts of the
+  // probabilities in column g and the low parts in column g + 8, which are
+  // added once at the end of the piece.
+  static_assert(!LO || (KV == KV_BF16 && !MQ), "low parts: bf16 cache, one new token");
+  constexpr bool lo_cols = LO;                     // the host launches LO only for G <= 8
+  const int qcol = lr < NC ? lr : ((lo_cols && lr >= 8 && lr < 8 + NC) ? lr - 8 : -1);
+  const bool lo_lane = lo_cols && qcol >= 0 && lr >= 8;   // carries the low parts of column qcol
+  const int lane_qi = MQ ? (qcol < 0 ? 0 : qcol) / G : 0;   // new token of this lane's column
   const int cap = p.max_blocks * BS;
 
   const int cost = p.piece_cost;
@@ -580,9 +607,9 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     // Rotated query of column lr at this lane's dims (fp32 RoPE from the
     // table): head g of new token qi (lr = qi * G + g) at position posn + qi.
     // Columns past the last load column 0 and are zeroed.
-    const int col = lr < NC ? lr : 0;
+    const int col = qcol < 0 ? 0 : qcol;
     const int hq = h * G + (col - lane_qi * G);
-    const bool hvalid = lr < NC;
+    const bool hvalid = qcol >= 0;
     const int64_t qrow = (((int64_t)b * TQ + lane_qi) * out_row_stride + hq) * D;
     const float* crow = p.rope_cos + (int64_t)(posn + lane_qi) * C::HALF;
     const float* srow = p.rope_sin + (int64_t)(posn + lane_qi) * C::HALF;
@@ -632,6 +659,12 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
         for (int i2 = 0; i2 < 4; ++i2) {
           w0[i2] = pack_bf16x2(y0[2 * i2], y0[2 * i2 + 1]);
           w1[i2] = pack_bf16x2(y1[2 * i2], y1[2 * i2 + 1]);
+          if (lo_cols && lo_lane) {   // the remainders (exact in fp32), rounded to bf16
+            w0[i2] = pack_bf16x2(y0[2 * i2] - __uint_as_float(w0[i2] << 16),
+                                 y0[2 * i2 + 1] - __uint_as_float(w0[i2] & 0xffff0000u));
+            w1[i2] = pack_bf16x2(y1[2 * i2] - __uint_as_float(w1[i2] << 16),
+                                 y1[2 * i2 + 1] - __uint_as_float(w1[i2] & 0xffff0000u));
+          }
         }
         qop.v[c] = __builtin_bit_cast(bf16x8_t, w0);
         if constexpr (C::KCH >= 2) qop.v[c + NPAIR] = __builtin_bit_cast(bf16x8_t, w1);
@@ -821,7 +854,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   auto softmax_pv = [&](f32x4_t a, TileRegs<C::KCH>& t, bool last) __attribute__((always_inline)) {
     float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = a[r] * sscale;
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (lo_cols) a[r] += swap_half_row(a[r]);   // the other half of the score
+      s[r] = a[r] * sscale;
+    }
     if (last || (cw.j == 0 && lo_tok > 16 * cw.lo) ||
         (MQ && 16 * (cw.j + cw.lo + 1) > L - TQ)) {
       const int t0 = 16 * (cw.j + cw.lo) + 4 * lq;   // token of this lane's first score
@@ -864,9 +900,16 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
       u32x2_t pw2;
       pw2[0] = pack_bf16x2(s[0], s[1]);
       pw2[1] = pack_bf16x2(s[2], s[3]);
-      const float ps = (__uint_as_float(pw2[0] << 16) + __uint_as_float(pw2[0] & 0xffff0000u)) +
-                       (__uint_as_float(pw2[1] << 16) + __uint_as_float(pw2[1] & 0xffff0000u));
+      const float h0 = __uint_as_float(pw2[0] << 16), h1 = __uint_as_float(pw2[0] & 0xffff0000u);
+      const float h2 = __uint_as_float(pw2[1] << 16), h3 = __uint_as_float(pw2[1] & 0xffff0000u);
+      // with low parts, the two columns of a pair together carry p to 16
+      // bits: the normaliser sums p itself; without, the rounded p
+      const float ps = lo_cols ? (s[0] + s[1]) + (s[2] + s[3]) : (h0 + h1) + (h2 + h3);
       l_run = __builtin_fmaf(l_run, alpha, ps);
+      if (lo_cols && lo_lane) {
+        pw2[0] = pack_bf16x2(s[0] - h0, s[1] - h1);
+        pw2[1] = pack_bf16x2(s[2] - h2, s[3] - h3);
+      }
       const s16x4_t pb = __builtin_bit_cast(s16x4_t, pw2);
 #pragma unroll
       for (int c = 0; c < C::KCH; ++c)
@@ -929,6 +972,12 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   };
 
   auto end_piece = [&]() __attribute__((always_inline)) {
+    if constexpr (lo_cols) {   // column g + 8 holds the low-part products of column g
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] += swap_half_row(acc[nt][r]);
+    }
     const float lt = sum_over_lq(l_run);
     if (!split) {
       store_out(cw.b, cw.h, acc, lt > 0.f ? vsc / lt : 0.f);
@@ -1246,14 +1295,20 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
       hipLaunchKernelGGL((decode_append_kernel<KV, D, BS>),
                          dim3((unsigned)((items + kBlockThreads / 64 - 1) / (kBlockThreads / 64))),
                          dim3(kBlockThreads), 0, stream, p);
-      hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, true>), dim3(p.n_waves / 4),
+      hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, true, false>), dim3(p.n_waves / 4),
                             dim3(kBlockThreads), 0, stream, ev ? ev[0] : nullptr,
                             ev ? ev[1] : nullptr, 0, p, p.block_tables, p.context_lens,
                             p.positions, static_cast<char*>(p.k_pool),
                             static_cast<char*>(p.v_pool));
     }
+  } else if (KV == KV_BF16 && p.group <= 8) {
+    hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, false, KV == KV_BF16>),
+                          dim3(p.n_waves / 4), dim3(kBlockThreads), 0, stream,
+                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, p, p.block_tables,
+                          p.context_lens, p.positions, static_cast<char*>(p.k_pool),
+                          static_cast<char*>(p.v_pool));
   } else {
-    hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, false>), dim3(p.n_waves / 4),
+    hipExtLaunchKernelGGL((decode_attn_kernel<KV, D, BS, false, false>), dim3(p.n_waves / 4),
                           dim3(kBlockThreads), 0, stream, ev ? ev[0] : nullptr,
                           ev ? ev[1] : nullptr, 0, p, p.block_tables, p.context_lens,
                           p.positions, static_cast<char*>(p.k_pool),
@@ -1266,8 +1321,8 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream, hipEvent_t* e
 
 template <int KV, int D, int BS>
 hipError_t occupancy_typed(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_attn_kernel<KV, D, BS, false>,
-                                                      kBlockThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks, decode_attn_kernel<KV, D, BS, false, false>, kBlockThreads, 0);
 }
 
 template <int KV, int D>
@@ -1281,40 +1336,25 @@ hipError_t dispatch_bs(int bs, const DecodeParams* p, hipStream_t stream, hipEve
   }
 }
 
-hipError_t dispatch(int kv_kind, int head_dim, int bs, const DecodeParams* p, hipStream_t stream,
-                    hipEvent_t* ev, int* blocks) {
-  switch (kv_kind * 1000 + head_dim) {
-    case KV_F32 * 1000 + 64:   return dispatch_bs<KV_F32, 64>(bs, p, stream, ev, blocks);
-    case KV_F32 * 1000 + 128:  return dispatch_bs<KV_F32, 128>(bs, p, stream, ev, blocks);
-    case KV_BF16 * 1000 + 64:  return dispatch_bs<KV_BF16, 64>(bs, p, stream, ev, blocks);
-    case KV_BF16 * 1000 + 128: return dispatch_bs<KV_BF16, 128>(bs, p, stream, ev, blocks);
-    case KV_FP8 * 1000 + 64:   return dispatch_bs<KV_FP8, 64>(bs, p, stream, ev, blocks);
-    case KV_FP8 * 1000 + 128:  return dispatch_bs<KV_FP8, 128>(bs, p, stream, ev, blocks);
+}  // namespace
+
+template <>
+hipError_t decode_dispatch<PKV_KV>(int head_dim, int block_size, const DecodeParams* p,
+                                   hipStream_t stream, hipEvent_t* events, int* blocks) {
+  switch (head_dim) {
+    case 64: return dispatch_bs<PKV_KV, 64>(block_size, p, stream, events, blocks);
+    case 128: return dispatch_bs<PKV_KV, 128>(block_size, p, stream, events, blocks);
     default: return hipErrorInvalidValue;
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
-                         hipStream_t stream, hipEvent_t* events) {
-  return dispatch(kv_kind, head_dim, block_size, &p, stream, events, nullptr);
-}
-
-int decode_ring_tiles(int kv_kind, int head_dim) {
-  switch (kv_kind * 1000 + head_dim) {
-    case KV_F32 * 1000 + 64:   return Cfg<KV_F32, 64, 16>::RING;
-    case KV_F32 * 1000 + 128:  return Cfg<KV_F32, 128, 16>::RING;
-    case KV_BF16 * 1000 + 64:  return Cfg<KV_BF16, 64, 16>::RING;
-    case KV_BF16 * 1000 + 128: return Cfg<KV_BF16, 128, 16>::RING;
-    case KV_FP8 * 1000 + 64:   return Cfg<KV_FP8, 64, 16>::RING;
-    case KV_FP8 * 1000 + 128:  return Cfg<KV_FP8, 128, 16>::RING;
+template <>
+int decode_ring_tiles_of<PKV_KV>(int head_dim) {
+  switch (head_dim) {
+    case 64: return Cfg<PKV_KV, 64, 16>::RING;
+    case 128: return Cfg<PKV_KV, 128, 16>::RING;
     default: return 0;
   }
-}
-
-hipError_t decode_occupancy(int kv_kind, int head_dim, int block_size, int* blocks) {
-  return dispatch(kv_kind, head_dim, block_size, nullptr, nullptr, nullptr, blocks);
 }
 
 }  // namespace pkv

@@ -4,15 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace pkv {
+#include "pkv_limits.h"
 
-constexpr int kGroupMax = 16;      // query heads per KV head the kernel serves
-constexpr int kMaxBatch = 4096;    // requests per step (LDS prefix array)
-constexpr int kWaveThreads = 64;
-constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
-constexpr int kTileTokens = 16;    // tokens per KV tile (the unit of work)
-constexpr int kMaxPieceCost = 64;  // work units a sequence start may cost
-constexpr int kWeightMinShare = 256;  // units per wavefront for uneven weights
+namespace pkv {
 
 enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
@@ -61,6 +55,24 @@ constexpr int partial_floats(int head_dim) { return 16 * head_dim + 2 * kGroupMa
 // `stream`; with `events` (4 of them), the start and stop of each kernel.
 hipError_t launch_decode(int kv_kind, int head_dim, int block_size, const DecodeParams& p,
                          hipStream_t stream, hipEvent_t* events);
+
+// The kernels of one cache type (each built in an object of its own): with
+// p, launch a step; without, the occupancy of the attention kernel in
+// *blocks.  And the tiles each wavefront keeps in flight.
+template <int KV>
+hipError_t decode_dispatch(int head_dim, int block_size, const DecodeParams* p, hipStream_t stream,
+                           hipEvent_t* events, int* blocks);
+template <> hipError_t decode_dispatch<KV_F32>(int, int, const DecodeParams*, hipStream_t,
+                                               hipEvent_t*, int*);
+template <> hipError_t decode_dispatch<KV_BF16>(int, int, const DecodeParams*, hipStream_t,
+                                                hipEvent_t*, int*);
+template <> hipError_t decode_dispatch<KV_FP8>(int, int, const DecodeParams*, hipStream_t,
+                                               hipEvent_t*, int*);
+template <int KV>
+int decode_ring_tiles_of(int head_dim);
+template <> int decode_ring_tiles_of<KV_F32>(int);
+template <> int decode_ring_tiles_of<KV_BF16>(int);
+template <> int decode_ring_tiles_of<KV_FP8>(int);
 
 // Tiles the attention kernel keeps in flight per wavefront (its load ring).
 int decode_ring_tiles(int kv_kind, int head_dim);
