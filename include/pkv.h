@@ -70,7 +70,11 @@ typedef enum pkv_status {
 typedef enum pkv_dtype {
   PKV_F32 = 0,               /* IEEE binary32 */
   PKV_BF16 = 1,              /* bfloat16 */
-  PKV_FP8_E4M3 = 2           /* OCP E4M3FN: bias 7, max 448, no inf */
+  PKV_FP8_E4M3 = 2,          /* OCP E4M3FN: bias 7, max 448, no inf */
+  /* Not a dtype: makes every int32 value a valid pkv_dtype, so that an
+   * unknown value from a C caller is refused (PKV_ERR_INVALID) rather than
+   * undefined behaviour in the C++ implementation. */
+  PKV_DTYPE_MAX_ENUM = 0x7fffffff
 } pkv_dtype;
 
 /* Opaque pool: owns the K and V block storage, the RoPE table, the FP8

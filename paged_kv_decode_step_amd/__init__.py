@@ -19,7 +19,7 @@ import torch  # noqa: F401  (binds libpkv to torch's HIP runtime, loaded first)
 __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
-    "EXPORTED_SYMBOLS", "BlockAllocator", "decode_step_multi", "stream_read",
+    "EXPORTED_SYMBOLS", "HOST_SYMBOLS", "BlockAllocator", "decode_step_multi", "stream_read",
     "decode_step_noalloc",
 ]
 
@@ -69,11 +69,23 @@ class _Info(ctypes.Structure):
     ]
 
 
+# the entry points that need no GPU: argument checks, the RoPE table, the
+# work-partition replay and the block allocator (a host-only build of the
+# library exports just these)
+HOST_SYMBOLS = (
+    "pkv_last_error", "pkv_check_decode_args", "pkv_rope_table_host", "pkv_plan_host",
+    "pkv_tile_tokens", "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats",
+    "pkv_alloc_refcount", "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
+    "pkv_alloc_prepare_step",
+)
+
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libpkv.so once and declare its signatures."""
+def load_library(path: str = LIB_PATH, host_only: bool = False):
+    """Load libpkv.so once and declare its signatures.  ``host_only`` loads
+    a build of the host-only entry points alone (``HOST_SYMBOLS``), such as
+    the sanitizer-instrumented one the CPU tests use."""
     global _lib
     if _lib is not None:
         return _lib
@@ -120,6 +132,8 @@ def load_library(path: str = LIB_PATH):
         "pkv_stream_read": (I32, [P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
+        if host_only and name not in HOST_SYMBOLS:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

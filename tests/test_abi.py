@@ -21,6 +21,7 @@ def header_functions():
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
 
 
+@pytest.mark.device_library
 def test_library_loads_and_exports_every_declared_function():
     lib = pkv.load_library()
     declared = header_functions()
@@ -70,6 +71,7 @@ def test_check_rejects(kw, code):
     assert pkv.last_error()
 
 
+@pytest.mark.device_library
 def test_pool_create_validates_before_touching_the_gpu():
     for args in [(0, 16, 8, 128, "bf16"), (10, 24, 8, 128, "bf16"),
                  (10, 16, 0, 128, "bf16"), (10, 16, 8, 80, "bf16"),
@@ -253,6 +255,7 @@ def test_partition_with_a_window_reads_only_the_window(window):
             assert n == -(-L // 16) - lo       # the tiles holding tokens [L - window, L)
 
 
+@pytest.mark.device_library
 def test_layout_and_rope_table_calls_check_their_arguments():
     """kv_pool_layout and kv_pool_rope_table through ctypes: a null pool or
     output pointer is refused with INVALID before anything is read."""
@@ -269,6 +272,7 @@ def test_layout_and_rope_table_calls_check_their_arguments():
     assert "null" in pkv.last_error()
 
 
+@pytest.mark.device_library
 def test_stream_read_checks_its_arguments():
     """pkv_stream_read refuses a null pointer or a size that is not a positive
     multiple of 16 before touching the GPU."""
