@@ -316,6 +316,86 @@ def allocator_bench(wl, device, steps: int) -> dict:
             "block_bytes": block_bytes}
 
 
+def timeline_summary(rec) -> dict:
+    """Where one step's attention kernel spent its time, from the
+    per-wavefront records of ``kv_pool_read_timeline`` (stamps of a 100 MHz
+    clock): when the wavefronts started (dispatch skew), how long each phase
+    took (median over the wavefronts with tiles), when they finished, and the
+    same per XCD.  Times in microseconds from the first wavefront's entry."""
+    rec = np.asarray(rec, dtype=np.int64)
+    t0 = rec[:, 0].min()
+    us = (rec[:, :6] - t0) / 100.0
+    tiles = rec[:, 6]
+    xcc = (rec[:, 7] >> 32) & 0xF
+    act = tiles > 0
+    a, ta, xa = us[act], tiles[act], xcc[act]
+    span = float(a[:, 5].max())
+    pc = lambda v, q: round(float(np.percentile(v, q)), 2)
+    med = lambda v: round(float(np.median(v)), 2)
+    loop = a[:, 4] - a[:, 3]
+    per_xcd = {}
+    for x in np.unique(xa):
+        m = xa == x
+        per_xcd[int(x)] = {"waves": int(m.sum()), "start_p50": med(a[m, 0]),
+                           "end_p50": med(a[m, 5]), "end_max": round(float(a[m, 5].max()), 2),
+                           "tiles_per_us_p50": round(float(np.median(ta[m] / np.maximum(loop[m], 1e-3))), 3)}
+    return {
+        "waves": int(len(rec)), "active": int(act.sum()), "span_us": round(span, 2),
+        "start_us": {"p50": pc(a[:, 0], 50), "p90": pc(a[:, 0], 90), "max": pc(a[:, 0], 100)},
+        "phase_us_p50": {"request_table": med(a[:, 1] - a[:, 0]), "tile_range": med(a[:, 2] - a[:, 1]),
+                         "ring_fill": med(a[:, 3] - a[:, 2]), "tile_loop": med(loop),
+                         "writes_and_exit": med(a[:, 5] - a[:, 4])},
+        "end_us": {"p10": pc(a[:, 5], 10), "p50": pc(a[:, 5], 50), "p90": pc(a[:, 5], 90),
+                   "max": round(span, 2)},
+        "busy_fraction": round(float((a[:, 5] - a[:, 0]).sum() / (len(a) * span)), 4),
+        "tiles_p50": med(ta), "per_xcd": per_xcd,
+    }
+
+
+def timeline_bench(args) -> dict:
+    """Run the timeline build of the library on the workload and summarise
+    the per-wavefront records of a few single steps."""
+    import torch
+    import paged_kv_decode_step_amd as pkv
+    import workloads
+
+    pkv.load_library(pkv.TIMELINE_LIB_PATH)
+    wl = workloads.make_workload(args.config)
+    pools, t, _ = setup_layers(wl, 1, "cuda:0")
+    pool = pools[0]
+    pool.set_window(args.window)
+    T = args.new_tokens
+    if T > 1:
+        dt = t["q"].dtype
+        gen = torch.Generator(device="cuda:0").manual_seed(1234)
+        c = wl.cfg
+        for w, h in (("q", c.n_q_heads), ("k_new", c.n_kv_heads), ("v_new", c.n_kv_heads)):
+            t[w] = torch.randn(wl.batch, T, h, c.head_dim, device="cuda:0", generator=gen).to(dt)
+        t["out"] = torch.empty_like(t["q"])
+        t["positions"] = (t["context_lens"] - T).contiguous()
+
+    def step():
+        if T > 1:
+            pkv.decode_step_multi(pool, t["q"], t["k_new"], t["v_new"], t["positions"],
+                                  t["block_tables"], t["context_lens"], t["out"])
+        else:
+            pkv.decode_step(pool, t["q"], t["k_new"], t["v_new"], t["positions"],
+                            t["block_tables"], t["context_lens"], t["out"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(max(1, args.steps)):
+        step()
+        reps.append(timeline_summary(pool.read_timeline()))
+    pool.close()
+    return {"metric": "attention kernel per-wavefront timeline (timeline build)",
+            "workload": wl.cfg.name, "window": args.window, "new_tokens": T,
+            "span_us_p50": round(float(np.median([r["span_us"] for r in reps])), 2),
+            "steps": reps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +416,10 @@ def main():
                          "workload's batch) and the device block copy, one JSON line")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the multi-layer step")
+    ap.add_argument("--timeline", action="store_true",
+                    help="run the timeline build of the library (libpkv_timeline.so) for "
+                         "--steps single steps after --warmup and print the per-wavefront "
+                         "phase summary of each, one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run --steps plain device copies of 1 GiB (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -343,6 +427,10 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+
+    if args.timeline:
+        print(json.dumps(timeline_bench(args)), flush=True)
+        return
 
     import torch
     import paged_kv_decode_step_amd as pkv

@@ -363,6 +363,23 @@ pkv_status kv_pool_enable_timing(pkv_pool* pool, int32_t enable);
 pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms,
                                int32_t* calls);
 
+/* Per-wavefront timeline of the last decode_step on this pool, from a
+ * timeline build of the library (libpkv_timeline.so, built with
+ * -DPKV_TIMELINE; the kernels are otherwise the same): where each attention
+ * wavefront's time went, the measurement that splits a step's duration into
+ * start-up, streaming and tail.  Synchronises the device, then copies
+ * min(capacity, n_waves) records of 8 uint64 to `records` (host memory):
+ * stamps of the GPU's constant 100 MHz clock at 0 entry, 1 request table
+ * built, 2 tile range found, 3 load ring filled, 4 tile loop done, 5 exit;
+ * 6 the wavefront's tiles; 7 HW_ID in the low word (bits 3:0 wave slot, 5:4
+ * SIMD, 11:8 compute unit, 15:13 shader engine) and XCC_ID in the high word.
+ * A wavefront without tiles records its entry in 0-5 and 0 tiles.
+ * *n_waves = wavefronts of the pool's launch.  decode_step_noalloc records
+ * nothing.  Errors: INVALID (null argument, capacity < 0), UNSUPPORTED (not
+ * a timeline build), HIP. */
+pkv_status kv_pool_read_timeline(pkv_pool* pool, uint64_t* records, int32_t capacity,
+                                 int32_t* n_waves);
+
 /* Read `bytes` of device memory at `src` once with the attention kernel's
  * 16-byte nontemporal loads, on the current device, asynchronously on
  * `stream` (NULL = the default stream): the bandwidth a plain streaming read

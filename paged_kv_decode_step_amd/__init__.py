@@ -20,10 +20,12 @@ __all__ = [
     "KVPool", "decode_step", "PkvError", "load_library", "LIB_PATH", "DTYPES",
     "check_decode_args", "rope_table_host", "plan_host", "tile_tokens",
     "EXPORTED_SYMBOLS", "HOST_SYMBOLS", "BlockAllocator", "decode_step_multi", "stream_read",
-    "decode_step_noalloc",
+    "decode_step_noalloc", "TIMELINE_LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# the same library with per-wavefront phase stamps (kv_pool_read_timeline)
+TIMELINE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv_timeline.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 _ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -42,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "pkv_alloc_create", "pkv_alloc_destroy", "pkv_alloc_stats", "pkv_alloc_refcount",
     "pkv_seq_add", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_info",
     "pkv_alloc_prepare_step", "pkv_stream_read", "decode_step_noalloc",
+    "kv_pool_read_timeline",
 )
 
 
@@ -130,6 +133,7 @@ def load_library(path: str = LIB_PATH, host_only: bool = False):
         "pkv_seq_info": (I32, [P, I32, IP, IP, IP, I32]),
         "pkv_alloc_prepare_step": (I32, [P, IP, I32, I32, IP, IP, IP, IP, I32, IP]),
         "pkv_stream_read": (I32, [P, I64, P, P]),
+        "kv_pool_read_timeline": (I32, [P, P, I32, IP]),
     }
     for name, (res, args) in sig.items():
         if host_only and name not in HOST_SYMBOLS:
@@ -226,6 +230,17 @@ class KVPool:
         _check(_lib.kv_pool_read_timing(self.handle, ctypes.byref(a), ctypes.byref(m),
                                         ctypes.byref(n)))
         return a.value, m.value, n.value
+
+    def read_timeline(self):
+        """``kv_pool_read_timeline``: the last step's per-wavefront records as
+        a uint64 array [n_waves, 8] (timeline builds only)."""
+        import numpy as np
+        cap = int(self.info()["n_waves"])
+        rec = np.zeros((cap, 8), dtype=np.uint64)
+        n = ctypes.c_int32()
+        _check(_lib.kv_pool_read_timeline(self.handle, ctypes.c_void_p(rec.ctypes.data), cap,
+                                          ctypes.byref(n)))
+        return rec[:min(cap, n.value)]
 
     def info(self) -> dict:
         inf = _Info()

@@ -1,9 +1,11 @@
 """Build ``libpkv.so`` (HIP kernels + C ABI) in-tree for gfx950.
 
-Usage: ``python -m paged_kv_decode_step_amd.build`` (or ``build()``).  The
-library lands next to this file, where the binding loads it from.  The
-sources compile to objects in parallel (the attention kernels once per cache
-type), which are then linked.
+Usage: ``python -m paged_kv_decode_step_amd.build [--timeline]`` (or
+``build()``).  The library lands next to this file, where the binding loads
+it from.  The sources compile to objects in parallel (the attention kernels
+once per cache type), which are then linked.  ``--timeline`` builds
+``libpkv_timeline.so`` instead: the same kernels with per-wavefront phase
+stamps (``kv_pool_read_timeline``), for measurement only.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
+TIMELINE_LIB = os.path.join(HERE, "libpkv_timeline.so")
+TIMELINE_OBJ_DIR = os.path.join(HERE, "_build_timeline")
 DECODE = os.path.join(CSRC, "decode.hip")
 KV_KINDS = (0, 1, 2)            # KV_F32, KV_BF16, KV_FP8: one object each
 OTHER_SOURCES = ["blocks.hip", "stream_read.hip", "noalloc.hip", "dispatch.cpp", "pkv_host.cpp",
@@ -40,9 +44,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def compile_jobs(decode_src: str = DECODE, obj_dir: str = OBJ_DIR) -> list:
+def compile_jobs(decode_src: str = DECODE, obj_dir: str = OBJ_DIR, defines=()) -> list:
     """(command, object) pairs: decode.hip once per cache type, then the rest."""
-    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC, *defines]
     jobs = []
     for kv in KV_KINDS:
         obj = os.path.join(obj_dir, f"decode_kv{kv}.o")
@@ -54,10 +58,13 @@ def compile_jobs(decode_src: str = DECODE, obj_dir: str = OBJ_DIR) -> list:
 
 
 def build(verbose: bool = False, decode_src: str = DECODE, out: str = LIB,
-          obj_dir: str = OBJ_DIR) -> str:
-    """Compile every source (in parallel) and link the shared library."""
+          obj_dir: str = OBJ_DIR, timeline: bool = False) -> str:
+    """Compile every source (in parallel) and link the shared library
+    (with ``timeline``, the timeline build at its own path)."""
+    if timeline and out == LIB:
+        out, obj_dir = TIMELINE_LIB, TIMELINE_OBJ_DIR
     os.makedirs(obj_dir, exist_ok=True)
-    jobs = compile_jobs(decode_src, obj_dir)
+    jobs = compile_jobs(decode_src, obj_dir, ["-DPKV_TIMELINE"] if timeline else [])
 
     def run(cmd):
         return subprocess.run(cmd, capture_output=True, text=True)
@@ -81,4 +88,4 @@ def build(verbose: bool = False, decode_src: str = DECODE, out: str = LIB,
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -84,6 +84,20 @@
 #define PKV_WAVES_PER_EU 2
 #endif
 
+// Timeline builds (-DPKV_TIMELINE, a separate library): every attention
+// wavefront records when it reached each phase of its work, from the GPU's
+// constant 100 MHz clock, into p.timeline[wave][8]: 0 entry, 1 request table
+// built in LDS, 2 tile range found, 3 load ring filled, 4 tile loop done,
+// 5 exit (after the queued writes), 6 its tiles, 7 HW_ID (low word: wave
+// slot, SIMD, CU, shader engine) and XCC_ID (high word).  A wavefront with
+// no tiles records its entry in slots 0-5 and 0 tiles.  Normal builds
+// compile none of this.
+#ifdef PKV_TIMELINE
+#define PKV_STAMP(i) const uint64_t stamp##i = __builtin_amdgcn_s_memrealtime()
+#else
+#define PKV_STAMP(i)
+#endif
+
 namespace pkv {
 namespace {
 
@@ -374,6 +388,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
+  PKV_STAMP(0);
   const int B = p.batch, hkv = p.n_kv_heads, G = p.group;
   const int TQ = MQ ? p.n_qtok : 1;           // new tokens per request
   const int NC = G * TQ;                      // MFMA columns in use (<= 16)
@@ -429,6 +444,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     if (tid == kBlockThreads - 1) sP[B] = run;
     __syncthreads();
   }
+  PKV_STAMP(1);
 
   // work units (< 2^31, checked on the host); U and W live in scalar
   // registers through the tile loop
@@ -437,8 +453,24 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
                                      WaveWeights{p.weight_first, p.weight_rest, p.n_first, p.weight_odd});
   const int64_t W = uniform((int)active_waves(U, p.n_waves, p.min_units, ww));
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
+#ifdef PKV_TIMELINE
+  auto record = [&](uint64_t s1, uint64_t s2, uint64_t s3, uint64_t s4, uint64_t s5, int tiles)
+      __attribute__((always_inline)) {
+    if (lane == 0 && p.timeline) {
+      uint64_t* r = p.timeline + (int64_t)wave * 8;
+      r[0] = stamp0; r[1] = s1; r[2] = s2; r[3] = s3; r[4] = s4; r[5] = s5;
+      r[6] = (uint64_t)tiles;
+      r[7] = (uint64_t)(uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4) |      // HW_ID
+             ((uint64_t)(uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 20) << 32);   // XCC_ID
+    }
+  };
+#define PKV_RECORD_IDLE() record(stamp0, stamp0, stamp0, stamp0, stamp0, 0)
+#else
+#define PKV_RECORD_IDLE()
+#endif
   if (wave >= W) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
+    PKV_RECORD_IDLE();
     return;
   }
   // The wave's tiles: those whose first unit lies in its unit range.
@@ -474,8 +506,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   }
   if (T <= 0) {
     if (lane == 0) p.headers[wave] = make_int4(0, 0, 0, 0);
+    PKV_RECORD_IDLE();
     return;
   }
+  PKV_STAMP(2);
 
   const int lane16 = lane * 16;
   const char* dummy = static_cast<const char*>(p.dummy);
@@ -1014,6 +1048,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     if (j0 == 0) split_seq = make_int4(cw.b, cw.h, cw.n, slot);
   };
 
+  PKV_STAMP(3);
   // ---- main loop: consume tile i from slot i % R, refill it with tile i + R.
   // Loads are issued unconditionally (past the range they read the dummy
   // buffer) so that the wait before each tile is a fixed count of the loads
@@ -1041,6 +1076,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     }, std::make_integer_sequence<int, R>{});
   }
 
+  PKV_STAMP(4);
   // ---- the queued writes, in order
   for (int off = 0; off < q_used;) {
     const u32x4_t hd = sQ[wid][off];
@@ -1089,6 +1125,10 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     split_hdr = make_int4(1, sb * hkv + sh, np, uniform(split_seq.w));
   }
   if (lane == 0) p.headers[wave] = split_hdr;
+#ifdef PKV_TIMELINE
+  PKV_STAMP(5);
+  record(stamp1, stamp2, stamp3, stamp4, stamp5, T);
+#endif
 }
 
 // Merge the partial softmax states of each split sequence (one wavefront per

@@ -27,6 +27,7 @@ struct DecodeParams {
   int4* headers;             // [n_waves] {split, request * Hkv + head, pieces, slot} of the
                              // split sequence whose first piece the wavefront holds
   const void* dummy;         // >= 8 KiB of readable device memory (tail loads)
+  uint64_t* timeline;        // [n_waves][8] per-wavefront phase stamps (timeline builds; else null)
   uint32_t* err;             // [4] range flags
   int32_t num_blocks;        // < 2^31 (checked at pool creation)
   int32_t batch;

@@ -29,6 +29,7 @@ int elem_bytes(pkv_dtype t) {
     case PKV_F32: return 4;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3: return 1;
+    case PKV_DTYPE_MAX_ENUM: break;
   }
   return 0;
 }
@@ -88,6 +89,7 @@ struct pkv_pool {
   bool has_scales = false;
   float* partials = nullptr;
   int4* headers = nullptr;         // per-wave split records (attention -> merge)
+  uint64_t* timeline = nullptr;    // [ws_waves][8] phase stamps (timeline builds only)
   void* dummy = nullptr;           // zeroed buffer read by loads past a wave's range
   uint32_t* err = nullptr;
   int64_t ws_bytes = 0;
@@ -139,6 +141,7 @@ static void free_pool(pkv_pool* p) {
   (void)hipFree(p->fp8_scales);
   (void)hipFree(p->partials);
   (void)hipFree(p->headers);
+  (void)hipFree(p->timeline);
   (void)hipFree(p->dummy);
   (void)hipFree(p->err);
   delete p;
@@ -165,6 +168,19 @@ static pkv_status size_workspace(pkv_pool* p, int waves_per_cu) {
     (void)hipFree(partials);
     return fail(PKV_ERR_OOM, "headers: %s", hipGetErrorString(e));
   }
+#ifdef PKV_TIMELINE
+  uint64_t* timeline = nullptr;
+  e = hipMalloc(&timeline, sizeof(uint64_t) * 8 * n_waves);
+  if (e == hipSuccess) e = hipMemset(timeline, 0, sizeof(uint64_t) * 8 * n_waves);
+  if (e != hipSuccess) {
+    (void)hipFree(partials);
+    (void)hipFree(headers);
+    (void)hipFree(timeline);
+    return fail(PKV_ERR_OOM, "timeline: %s", hipGetErrorString(e));
+  }
+  if (p->timeline) p->retired.push_back(p->timeline);
+  p->timeline = timeline;
+#endif
   if (p->partials) p->retired.push_back(p->partials);
   if (p->headers) p->retired.push_back(p->headers);
   p->partials = partials;
@@ -565,6 +581,7 @@ static pkv_status launch_step(pkv_pool* pool, const void* q, const void* k_new,
   p.partials = fixed ? fixed->partials : pool->partials;
   p.headers = fixed ? fixed->headers : pool->headers;
   p.dummy = pool->dummy;
+  p.timeline = fixed ? nullptr : pool->timeline;
   p.err = pool->err;
   p.num_blocks = (int32_t)pool->num_blocks;
   p.batch = batch;
@@ -667,6 +684,22 @@ pkv_status kv_pool_read_timing(pkv_pool* pool, double* attn_ms, double* merge_ms
   *merge_ms = m;
   *calls = pool->timed_calls;
   pool->timed_calls = 0;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_read_timeline(pkv_pool* pool, uint64_t* records, int32_t capacity,
+                                 int32_t* n_waves) {
+  if (!pool || !records || !n_waves) return fail(PKV_ERR_INVALID, "null argument");
+  if (capacity < 0) return fail(PKV_ERR_INVALID, "capacity must be >= 0");
+  if (!pool->timeline)
+    return fail(PKV_ERR_UNSUPPORTED, "not a timeline build (libpkv_timeline.so records the timeline)");
+  DeviceGuard g(pool->device);
+  hipError_t e = hipDeviceSynchronize();
+  const int32_t n = std::min(capacity, pool->n_waves);
+  if (e == hipSuccess && n > 0)
+    e = hipMemcpy(records, pool->timeline, sizeof(uint64_t) * 8 * n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the timeline");
+  *n_waves = pool->n_waves;
   return PKV_OK;
 }
 

@@ -282,3 +282,24 @@ def test_stream_read_checks_its_arguments():
     assert lib.pkv_stream_read(ctypes.c_void_p(0x1000), 1000, ctypes.c_void_p(0x2000), None) == INVALID
     assert lib.pkv_stream_read(ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x2000), None) == INVALID
     assert lib.pkv_stream_read(ctypes.c_void_p(0x1008), 1024, ctypes.c_void_p(0x2000), None) == INVALID
+
+
+@pytest.mark.device_library
+def test_read_timeline_checks_its_arguments():
+    """kv_pool_read_timeline refuses a null pool or output with INVALID
+    before anything is read."""
+    import ctypes
+    lib = pkv.load_library()
+    n = ctypes.c_int32()
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.kv_pool_read_timeline(None, buf, 1, ctypes.byref(n)) == INVALID
+    assert "null" in pkv.last_error()
+
+
+@pytest.mark.device_library
+@pytest.mark.skipif(not os.path.exists(pkv.TIMELINE_LIB_PATH), reason="timeline build not present")
+def test_timeline_build_exports_the_same_functions():
+    import ctypes
+    lib = ctypes.CDLL(pkv.TIMELINE_LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name

@@ -1,0 +1,49 @@
+"""The timeline build (libpkv_timeline.so): the same kernels with
+per-wavefront phase stamps.  Its step matches the oracle like the normal
+build's, and every wavefront's record is whole and ordered; the normal
+build refuses to read a timeline."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import paged_kv_decode_step_amd as pkv
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_normal_build_has_no_timeline():
+    import gpu_problem as gp
+    import problem
+    import workloads
+    wl = workloads.custom_workload([5, 40], n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                   block_size=16, kv_dtype="bf16", io_dtype="bf16", seed=3)
+    run = gp.Run(wl, problem.build(wl)).step()
+    try:
+        with pytest.raises(pkv.PkvError, match="UNSUPPORTED"):
+            run.pool.read_timeline()
+    finally:
+        run.close()
+
+
+@pytest.mark.skipif(not os.path.exists(pkv.TIMELINE_LIB_PATH),
+                    reason="timeline build not present (python -m paged_kv_decode_step_amd.build --timeline)")
+def test_timeline_build_matches_oracle_and_records_every_wavefront():
+    res = subprocess.run([sys.executable, os.path.join(HERE, "timeline_child.py")],
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+    d = json.loads(res.stdout.strip().splitlines()[-1])
+    assert d["err"] <= d["tol"], d["err"]
+    rec = np.array(d["records"], dtype=np.int64)
+    assert rec.shape == (d["n_waves"], 8)
+    stamps, tiles = rec[:, :6], rec[:, 6]
+    assert (stamps[:, 0] > 0).all()                      # every wavefront recorded its entry
+    assert (np.diff(stamps, axis=1) >= 0).all()          # phases in order
+    assert tiles.sum() == d["tiles_expected"]            # every tile belongs to one wavefront
+    assert ((rec[:, 7] >> 32) & 0xF).max() < 8           # XCC ids
+    span = (stamps[:, 5].max() - stamps[:, 0].min()) / 100.0
+    assert 0.0 < span < 10_000.0                         # microseconds, one small step
