@@ -354,7 +354,8 @@ def timeline_summary(rec) -> dict:
 
 def timeline_bench(args) -> dict:
     """Run the timeline build of the library on the workload and summarise
-    the per-wavefront records of a few single steps."""
+    the per-wavefront records of a few steps, each launched right behind
+    another step."""
     import torch
     import paged_kv_decode_step_amd as pkv
     import workloads
@@ -387,6 +388,10 @@ def timeline_bench(args) -> dict:
     torch.cuda.synchronize()
     reps = []
     for _ in range(max(1, args.steps)):
+        # two steps back to back: the records are the second's, a step
+        # launched behind another as in a decode loop (reading them
+        # synchronises, so a single step would start on an idle GPU)
+        step()
         step()
         reps.append(timeline_summary(pool.read_timeline()))
     pool.close()
