@@ -47,3 +47,22 @@ def test_timeline_build_matches_oracle_and_records_every_wavefront():
     assert ((rec[:, 7] >> 32) & 0xF).max() < 8           # XCC ids
     span = (stamps[:, 5].max() - stamps[:, 0].min()) / 100.0
     assert 0.0 < span < 10_000.0                         # microseconds, one small step
+
+
+@pytest.mark.skipif(not os.path.exists(pkv.TIMELINE_LIB_PATH),
+                    reason="timeline build not present (python -m paged_kv_decode_step_amd.build --timeline)")
+def test_bench_timeline_mode_summarises_a_step():
+    """``bench.py --timeline`` on the small ragged workload: one JSON line
+    whose phases are ordered and whose wavefronts with tiles hold them all."""
+    root = os.path.dirname(HERE)
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--timeline", "--config", "1",
+                          "--steps", "2", "--warmup", "2"],
+                         capture_output=True, text=True, timeout=300, cwd=root)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+    d = json.loads(res.stdout.strip().splitlines()[-1])
+    assert d["workload"].startswith("tiny_ragged") and len(d["steps"]) == 2
+    for s in d["steps"]:
+        assert s["active"] >= 1 and s["span_us"] > 0
+        assert all(v >= 0 for v in s["phase_us_p50"].values())
+        e = s["end_us"]
+        assert e["p10"] <= e["p50"] <= e["p90"] <= e["max"] == s["span_us"]
