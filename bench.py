@@ -316,6 +316,15 @@ def allocator_bench(wl, device, steps: int) -> dict:
             "block_bytes": block_bytes}
 
 
+def make_bench_workload(args):
+    """The workload of ``--config``, or one GPU's head shard of it with
+    ``--tp`` above 1."""
+    import workloads
+    if args.tp > 1:
+        return workloads.shard_workload(args.config, args.tp)
+    return workloads.make_workload(args.config)
+
+
 def timeline_summary(rec) -> dict:
     """Where one step's attention kernel spent its time, from the
     per-wavefront records of ``kv_pool_read_timeline`` (stamps of a 100 MHz
@@ -361,7 +370,7 @@ def timeline_bench(args) -> dict:
     import workloads
 
     pkv.load_library(pkv.TIMELINE_LIB_PATH)
-    wl = workloads.make_workload(args.config)
+    wl = make_bench_workload(args)
     pools, t, _ = setup_layers(wl, 1, "cuda:0")
     pool = pools[0]
     pool.set_window(args.window)
@@ -416,6 +425,10 @@ def main():
                     help="sliding-window attention over the last W tokens (0 = whole context)")
     ap.add_argument("--new-tokens", type=int, default=1,
                     help="T new tokens per request (decode_step_multi; the lengths count them)")
+    ap.add_argument("--tp", type=int, default=1,
+                    help="measure one GPU's shard of the workload when its heads are split over "
+                         "TP GPUs (Hkv/TP KV heads and their query heads, same requests); the "
+                         "run itself stays on one GPU")
     ap.add_argument("--allocator", action="store_true",
                     help="only measure the block allocator's host step (prepare_step for the "
                          "workload's batch) and the device block copy, one JSON line")
@@ -452,7 +465,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}), flush=True)
         return
-    wl = workloads.make_workload(args.config)
+    wl = make_bench_workload(args)
     c = wl.cfg
     if args.allocator:
         print(json.dumps(allocator_bench(wl, device, args.steps)), flush=True)
@@ -571,7 +584,7 @@ def main():
                    "block_size": c.block_size, "kv_dtype": c.kv_dtype,
                    "io_dtype": c.io_dtype, "mean_context": float(wl.context_lens.mean()),
                    "pool_copies": n_layers, "window": args.window,
-                   "new_tokens": args.new_tokens},
+                   "new_tokens": args.new_tokens, "tp_shard": args.tp},
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s_per_layer": round(wl.batch * T / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,

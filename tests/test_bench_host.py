@@ -61,3 +61,29 @@ def test_traffic_is_reported_only_for_the_kernel_it_was_measured_on(monkeypatch)
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.measured_traffic(name, 1.0) is None
     assert bench.measured_traffic("no_such_workload", 1.0) is None
+
+
+@pytest.mark.parametrize("k,tp", [(3, 8), (5, 8), (2, 4)])
+def test_tensor_parallel_shard_keeps_the_requests_and_splits_the_heads(k, tp):
+    """``--tp``: one GPU's share keeps every request, length and block table
+    and holds Hkv/tp KV heads with their Hq/tp query heads (the same group),
+    so its algorithmic bytes are the KV and head-proportional terms over tp."""
+    full, shard = workloads.make_workload(k), workloads.shard_workload(k, tp)
+    assert shard.cfg.n_kv_heads * tp == full.cfg.n_kv_heads
+    assert shard.cfg.n_q_heads * tp == full.cfg.n_q_heads
+    assert shard.cfg.group == full.cfg.group
+    assert (shard.context_lens == full.context_lens).all()
+    assert (shard.block_tables == full.block_tables).all()
+    assert shard.num_blocks == full.num_blocks and shard.cfg.name.endswith(f"_tp{tp}shard")
+    c = full.cfg
+    per_batch = int((4 * ((full.context_lens.astype("int64") + c.block_size - 1) // c.block_size) + 8).sum())
+    rope = full.batch * c.head_dim * 4
+    head_part = bench.algorithmic_bytes(full) - per_batch - rope
+    assert bench.algorithmic_bytes(shard) == head_part // tp + per_batch + rope
+
+
+def test_tensor_parallel_shard_needs_divisible_heads():
+    with pytest.raises(ValueError):
+        workloads.shard_workload(1, 8)          # 4 KV heads
+    with pytest.raises(ValueError):
+        workloads.shard_workload(2, 3)

@@ -135,8 +135,8 @@ def oracle_every_request(wl, pool, got, io, scales, window=0):
     return errs
 
 
-def run_full(k, window=0):
-    wl = workloads.make_workload(k)
+def run_full(k, window=0, tp=1):
+    wl = workloads.shard_workload(k, tp) if tp > 1 else workloads.make_workload(k)
     c = wl.cfg
     print(f"full-size parity: workload {c.name}, {wl.batch} requests, {wl.num_blocks} blocks"
           + (f", window {window}" if window else ""), flush=True)
@@ -170,6 +170,14 @@ def run_full(k, window=0):
 @pytest.mark.parametrize("k", [3, 4, 5])
 def test_full_size_every_request(k):
     run_full(k)
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_full_size_tensor_parallel_shard(k):
+    """One GPU's share of the 70B-shaped and the mixed B=512 workloads when
+    their heads are split over 8 GPUs (8 query heads, 1 KV head, the same
+    requests), as ``bench.py --tp 8`` runs it."""
+    run_full(k, tp=8)
 
 
 def test_full_size_window():

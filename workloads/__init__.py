@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "Workload", "make_workload", "custom_workload",
-    "host_normals", "device_normals",
+    "shard_workload", "host_normals", "device_normals",
 ]
 
 
@@ -175,6 +175,27 @@ def make_workload(cfg_or_index, batch: Optional[int] = None) -> Workload:
     lens32 = lens.astype(np.int32)
     return Workload(cfg, lens32, (lens32 - 1).astype(np.int32), tables,
                     num_blocks, ch)
+
+
+def shard_workload(cfg_or_index, tp: int) -> Workload:
+    """One GPU's share of a workload when its attention heads are split over
+    ``tp`` GPUs: tensor parallelism, which runs a 70B model over 8 GPUs
+    ("Lesson 13.17 TensorRT-LLM: NVIDIA's Optimized Inference Engine", section
+    "Speculative decoding and running one model across many GPUs") by
+    splitting the attention projections across them ("TensorRT-LLM Guide:
+    High-Throughput GPU Inference Engine", section "1. Scaling Across NVLink
+    with Tensor Parallelism (TP)").  The same requests, lengths and block
+    tables, with ``Hkv / tp`` KV heads and their ``Hq / tp`` query heads; the
+    shard's cache and new values are drawn from the same streams at the
+    shard's shape."""
+    cfg = CONFIGS[cfg_or_index] if isinstance(cfg_or_index, int) else cfg_or_index
+    if tp < 1 or cfg.n_kv_heads % tp or cfg.n_q_heads % tp:
+        raise ValueError(f"{cfg.name}: {cfg.n_q_heads}/{cfg.n_kv_heads} heads do not split over {tp}")
+    full = make_workload(cfg)
+    shard = dataclasses.replace(cfg, name=f"{cfg.name}_tp{tp}shard", n_q_heads=cfg.n_q_heads // tp,
+                                n_kv_heads=cfg.n_kv_heads // tp)
+    return Workload(shard, full.context_lens, full.positions, full.block_tables,
+                    full.num_blocks, full.seeds)
 
 
 def custom_workload(lengths: Sequence[int], *, n_q_heads: int, n_kv_heads: int,
