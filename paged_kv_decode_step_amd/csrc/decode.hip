@@ -1143,17 +1143,32 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 #endif
 }
 
-// Merge the partial softmax states of each split sequence (one wavefront per
-// sequence, found from the header its first wavefront left):
+// Merge the partial softmax states of each split sequence, found from the
+// header its first wavefront left:
 // out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
-// A piece's accumulators are G*D floats in [head][dim] order; lane l takes
-// the 16-byte chunks l + 64k (k < KC) of every piece, so all 64 lanes work
-// and a batch of 32/KC pieces is in flight at once, with the running maximum
+// A piece's accumulators are G*D floats in [head][dim] order, 16-byte
+// chunks of which lane l takes l + 64c.  Each lane has KC load slots per
+// piece and a batch holds 32/KC pieces in flight, with the running maximum
 // rescaling the sums between batches.
+//
+// A sequence of many pieces (a long request spread over many wavefronts)
+// would take its merge wavefront one round trip per batch.  From kShareMin
+// pieces on (more than one batch), the merge wavefronts of the kHelpers
+// wavefronts after its first one, each of which holds only a middle piece of
+// it and so has no header of its own, share the work by columns: merge
+// wavefront j of the 1 + kHelpers takes the j-th quarter of the chunks of
+// every piece and writes those output elements.  No two write the same
+// element and none waits for another.  With a quarter of the chunks a lane
+// needs nc = 2^lkp slots per piece, and its other slots hold further pieces
+// (R = KC / nc per batch slot), whose partial sums are combined at the end.
 template <bool IO_BF16, int D, int KC>
 __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParams p) {
   constexpr int PF = partial_floats(D);
-  constexpr int PPB = 32 / KC;                  // pieces per batch
+  constexpr int PPB = 32 / KC;                  // batch slots of pieces
+  constexpr int kHelpers = 3;
+  // pieces from which the merge is shared: more than one batch, and enough
+  // that wavefronts 1..kHelpers after the first hold middle pieces
+  constexpr int kShareMin = PPB + 1 > kHelpers + 2 ? PPB + 1 : kHelpers + 2;
   const int lane = threadIdx.x & 63;
   const int G = p.group, hkv = p.n_kv_heads, TQ = p.n_qtok;
   // With several new tokens per request, merge wavefront mw takes the G
@@ -1162,37 +1177,75 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
   const int mw = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   const int w = TQ > 1 ? mw / TQ : mw;
   const int qi = TQ > 1 ? mw - w * TQ : 0;
-  const int4 hdr = p.headers[w];
-  if (!uniform(hdr.x)) return;
-  const int seq = uniform(hdr.y), np = uniform(hdr.z), slot0 = uniform(hdr.w);
+  // this wavefront's header and the kHelpers before it, in one round trip
+  int4 hj[kHelpers + 1];
+#pragma unroll
+  for (int j = 0; j <= kHelpers; ++j) hj[j] = w - j >= 0 ? p.headers[w - j] : make_int4(0, 0, 0, 0);
+  int ws = -1, part = 0, nparts = 1, seq = 0, np = 0, slot0 = 0;
+  if (uniform(hj[0].x)) {
+    ws = w;
+    seq = uniform(hj[0].y);
+    np = uniform(hj[0].z);
+    slot0 = uniform(hj[0].w);
+    nparts = np >= kShareMin ? kHelpers + 1 : 1;
+  } else {
+#pragma unroll
+    for (int j = 1; j <= kHelpers; ++j) {
+      if (ws < 0 && uniform(hj[j].x) && uniform(hj[j].z) >= kShareMin) {
+        ws = w - j;
+        part = j;
+        nparts = kHelpers + 1;
+        seq = uniform(hj[j].y);
+        np = uniform(hj[j].z);
+        slot0 = uniform(hj[j].w);
+      }
+    }
+  }
+  if (ws < 0) return;
   const int b = seq / hkv, h = seq - (seq / hkv) * hkv;
-  const int nchunk = G * D / 4;               // query head x D of new token qi
+  const int nchunk = G * D / 4;               // query head x D of new token qi (a multiple of 16)
   const int cbase = qi * nchunk;              // its first chunk in a piece
-  int ch[KC], hd[KC];
-  bool ok[KC];
+  // piece pc's partial state: slot slot0 of wavefront ws for pc = 0, slot 0
+  // of wavefront ws + pc after it
+  const float* part0 = p.partials + (int64_t)ws * 2 * PF;
+  auto piece = [&](int pc) __attribute__((always_inline)) -> const float* {
+    return part0 + (pc == 0 ? slot0 * PF : pc * (2 * PF));
+  };
+  auto write_out = [&](int c, const f32x4_t& nsum, float dsum) __attribute__((always_inline)) {
+    const float inv = dsum > 0.f ? 1.0f / dsum : 0.f;
+    const int hc = (4 * c) / D;
+    const int d = 4 * c - hc * D;
+    const int64_t row = (((int64_t)b * TQ + qi) * hkv * G + h * G + hc) * D;
+    if constexpr (IO_BF16) {
+      u32x2_t o;
+      o[0] = bf16_rne(nsum[0] * inv) | (bf16_rne(nsum[1] * inv) << 16);
+      o[1] = bf16_rne(nsum[2] * inv) | (bf16_rne(nsum[3] * inv) << 16);
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = o;
+    } else {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = nsum * inv;
+    }
+  };
   float M[KC], den[KC];
   f32x4_t num[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    ch[k] = lane + 64 * k;
-    ok[k] = ch[k] < nchunk;
-    hd[k] = ok[k] ? (4 * ch[k]) / D : 0;
     M[k] = -INFINITY;
     den[k] = 0.f;
     num[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  for (int k0 = 0; k0 < np; k0 += PPB) {
+  // one batch of pieces: slot (j, k) holds chunk ch[k] of piece pc0 + pstep * j + poff[k]
+  auto batch = [&](int pc0, int pstep, const int (&poff)[KC], const int (&ch)[KC],
+                   const int (&hd)[KC], const bool (&ok)[KC]) __attribute__((always_inline)) {
     f32x4_t a[PPB][KC];
     f32x2_t ml[PPB][KC];
 #pragma unroll
     for (int j = 0; j < PPB; ++j) {
-      const int pc = min(k0 + j, np - 1);
-      const float* part = p.partials + ((int64_t)(w + pc) * 2 + (pc == 0 ? slot0 : 0)) * PF;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
-        a[j][k] = ok[k] ? *reinterpret_cast<const f32x4_t*>(part + 4 * (cbase + ch[k]))
+        const float* pp = piece(min(pc0 + pstep * j + poff[k], np - 1));
+        a[j][k] = ok[k] ? *reinterpret_cast<const f32x4_t*>(pp + 4 * (cbase + ch[k]))
                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        ml[j][k] = *reinterpret_cast<const f32x2_t*>(part + 16 * D + 2 * (qi * G + hd[k]));
+        ml[j][k] = *reinterpret_cast<const f32x2_t*>(pp + 16 * D + 2 * (qi * G + hd[k]));
       }
     }
 #pragma unroll
@@ -1200,14 +1253,14 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
       float mb = M[k];
 #pragma unroll
       for (int j = 0; j < PPB; ++j)
-        if (k0 + j < np) mb = fmaxf(mb, ml[j][k][0]);
+        if (pc0 + pstep * j + poff[k] < np) mb = fmaxf(mb, ml[j][k][0]);
       const float base = mb == -INFINITY ? 0.f : mb;
       const float sc = exp2_fast(M[k] - base);
       den[k] *= sc;
       num[k] *= sc;
 #pragma unroll
       for (int j = 0; j < PPB; ++j) {
-        if (k0 + j < np) {
+        if (pc0 + pstep * j + poff[k] < np) {
           const float f = exp2_fast(ml[j][k][0] - base);
           den[k] = __builtin_fmaf(f, ml[j][k][1], den[k]);
           num[k] += f * a[j][k];
@@ -1215,21 +1268,61 @@ __global__ __launch_bounds__(kBlockThreads) void decode_merge_kernel(DecodeParam
       }
       M[k] = mb;
     }
+  };
+  int ch[KC], hd[KC], poff[KC];
+  bool ok[KC];
+  if (nparts == 1) {
+    // the whole sequence here: slot (j, k) holds chunk lane + 64k of piece k0 + j
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      ch[k] = lane + 64 * k;
+      ok[k] = ch[k] < nchunk;
+      hd[k] = ok[k] ? (4 * ch[k]) / D : 0;
+      poff[k] = 0;
+    }
+    for (int k0 = 0; k0 < np; k0 += PPB) batch(k0, 1, poff, ch, hd, ok);
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (ok[k]) write_out(ch[k], num[k], den[k]);
+    return;
   }
+  // a share of the columns: nsh chunks from c_lo, 2^lkp per lane; slot (j, k)
+  // holds chunk c_lo + lane + 64 (k mod 2^lkp) of piece k0 + R j + (k >> lkp)
+  const int nsh = nchunk / nparts;
+  const int c_lo = part * nsh;
+  int lkp = 0;
+  while ((64 << lkp) < nsh) ++lkp;
+  const int nc = 1 << lkp, R = KC >> lkp;
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    if (!ok[k]) continue;
-    const float inv = den[k] > 0.f ? 1.0f / den[k] : 0.f;
-    const int d = 4 * ch[k] - hd[k] * D;
-    const int64_t row = (((int64_t)b * TQ + qi) * hkv * G + h * G + hd[k]) * D;
-    if constexpr (IO_BF16) {
-      u32x2_t o;
-      o[0] = bf16_rne(num[k][0] * inv) | (bf16_rne(num[k][1] * inv) << 16);
-      o[1] = bf16_rne(num[k][2] * inv) | (bf16_rne(num[k][3] * inv) << 16);
-      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + row + d) = o;
-    } else {
-      *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + row + d) = num[k] * inv;
+    const int within = lane + 64 * (k & (nc - 1));
+    ok[k] = within < nsh;
+    ch[k] = c_lo + (ok[k] ? within : 0);
+    hd[k] = (4 * ch[k]) / D;
+    poff[k] = k >> lkp;
+  }
+  for (int k0 = 0; k0 < np; k0 += PPB * R) batch(k0, R, poff, ch, hd, ok);
+  // slot k's sums cover chunk k mod nc over its own pieces: combine the
+  // slots of each chunk
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    if (k >= nc || !ok[k]) continue;
+    float mc = -INFINITY;
+#pragma unroll
+    for (int k2 = 0; k2 < KC; ++k2)
+      if ((k2 & (nc - 1)) == k) mc = fmaxf(mc, M[k2]);
+    const float base = mc == -INFINITY ? 0.f : mc;
+    float dsum = 0.f;
+    f32x4_t nsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < KC; ++k2) {
+      if ((k2 & (nc - 1)) == k) {
+        const float f = exp2_fast(M[k2] - base);
+        dsum = __builtin_fmaf(f, den[k2], dsum);
+        nsum += f * num[k2];
+      }
     }
+    write_out(ch[k], nsum, dsum);
   }
 }
 

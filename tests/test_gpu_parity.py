@@ -105,6 +105,23 @@ def test_many_splits_and_no_split_agree(kv):
         assert gp.row_rel_err(out_a, other).max() <= gp.tolerance(kv)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_single_long_request_spread_over_many_wavefronts(kv):
+    """One 32768-token request with one KV head: its one sequence is cut into
+    over a hundred pieces, whose merge the first piece's merge wavefront
+    shares by columns with the three after it."""
+    run_and_check(small([32768], kv=kv, hq=8, hkv=1))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("min_units", [16, 3])
+def test_long_and_short_sequences_with_many_pieces(kv, min_units):
+    """Long sequences (tens to hundreds of pieces each, shared merges) next to
+    short ones, at two piece sizes."""
+    run_and_check(small([20000, 10, 8000, 3, 3000, 1], kv=kv, hq=16, hkv=2),
+                  waves_per_cu=8, min_units=min_units)
+
+
 def test_block_permutation_is_bit_exact_on_gpu():
     wl = small([77, 300, 5, 1200], kv="bf16")
     arrs = problem.build(wl)
