@@ -424,15 +424,36 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
 
   const int cost = p.piece_cost;
   // ---- work units per request (hkv sequences of tiles + cost each),
-  // prefix-summed into LDS (every workgroup)
-  for (int i = tid; i < B; i += kBlockThreads) {
-    const int Li = lens[i];
-    const int lo = window_first_tile(Li, cap, p.window);
-    sLo[i] = lo;
-    sP[i] = hkv * (tiles_of(Li, cap) - lo + cost);
-  }
-  __syncthreads();
-  {
+  // prefix-summed into LDS (every workgroup).  Up to 64 requests, every
+  // wavefront builds the whole table itself, one request per lane with a
+  // wave-wide prefix sum, and reads back only what it wrote itself, so no
+  // workgroup barrier holds it back (the four write the same values).
+  int lane_p = 0;                      // with B <= 64: P[lane], the first unit of request lane
+  if (B <= 64) {
+    int u = 0;
+    if (lane < B) {
+      const int Li = lens[lane];
+      const int lo = window_first_tile(Li, cap, p.window);
+      u = hkv * (tiles_of(Li, cap) - lo + cost);
+      sLo[lane] = lo;
+    }
+    int incl = u;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    lane_p = incl - u;
+    if (lane < B) sP[lane] = lane_p;
+    if (lane == B - 1) sP[B] = incl;
+  } else {
+    for (int i = tid; i < B; i += kBlockThreads) {
+      const int Li = lens[i];
+      const int lo = window_first_tile(Li, cap, p.window);
+      sLo[i] = lo;
+      sP[i] = hkv * (tiles_of(Li, cap) - lo + cost);
+    }
+    __syncthreads();
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int i0 = tid * per;
     int sum = 0;
@@ -496,9 +517,19 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
     const int end = lane & 1;
     const int64_t x = wave_start(wave + end, U, W, ww);
     int64_t g = (int64_t)sP[B] - (int64_t)hkv * cost * B;        // all tiles
+    // With B <= 64 the request holding unit x is found with one ballot per
+    // end over the lanes' P[lane] (the units are below 2^31): the number of
+    // requests whose first unit is <= x, less one.  Else a binary search.
+    int rq = 0;
+    if (B <= 64) {
+      const int x0 = __builtin_amdgcn_readlane((int)x, 0), x1 = __builtin_amdgcn_readlane((int)x, 1);
+      const int n0 = __popcll(__ballot(lane < B && lane_p <= x0));
+      const int n1 = __popcll(__ballot(lane < B && lane_p <= x1));
+      rq = (end ? n1 : n0) - 1;
+    }
     TilePos t = {0, 0, 0, 1};
     if (x < U) {
-      t = tile_at_unit(sP, B, hkv, cost, x);
+      t = B <= 64 ? tile_in_request(sP, rq, hkv, cost, x) : tile_at_unit(sP, B, hkv, cost, x);
       g = global_tile(sP, t.b, t.h, t.j, t.n, hkv, cost);
     }
     const int g0 = __builtin_amdgcn_readlane((int)g, 0);     // tile counts < 2^31
