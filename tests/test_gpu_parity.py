@@ -122,6 +122,15 @@ def test_long_and_short_sequences_with_many_pieces(kv, min_units):
                   waves_per_cu=8, min_units=min_units)
 
 
+@pytest.mark.parametrize("batch", [63, 64, 65])
+def test_batches_around_the_per_wavefront_request_table(batch):
+    """Up to 64 requests every wavefront builds the request table and finds
+    its requests by ballot; from 65 on the workgroup builds it in LDS: both
+    sides of the boundary, ragged lengths, against the oracle."""
+    lens = np.random.default_rng(batch).integers(1, 700, size=batch)
+    run_and_check(small(lens.tolist(), kv="bf16", hq=16, hkv=4))
+
+
 def test_block_permutation_is_bit_exact_on_gpu():
     wl = small([77, 300, 5, 1200], kv="bf16")
     arrs = problem.build(wl)
