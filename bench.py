@@ -60,6 +60,29 @@ def algorithmic_bytes(wl, window: int = 0, new_tokens: int = 1) -> int:
     return total
 
 
+def attention_flops(wl, window: int = 0, new_tokens: int = 1) -> int:
+    """Multiply-adds of the step's attention, counted as 2 FLOPs each: the
+    scores q.K and the weighted sum p.V, D each, for every query head and
+    every token it attends to (the whole context, its last ``window`` tokens
+    with a window, or causally the first L - T + i + 1 for new token i of T)."""
+    c = wl.cfg
+    L = wl.context_lens.astype(np.int64)
+    T = new_tokens
+    attended = np.zeros_like(L)
+    for i in range(T):
+        n = L - T + i + 1
+        attended += np.minimum(n, window) if window > 0 else n
+    return int(4 * c.n_q_heads * c.head_dim * attended.sum())
+
+
+# Context from the pages (another GPU, another path: not a target): "TensorRT-LLM
+# Guide: High-Throughput GPU Inference Engine", section "1. The Arithmetic
+# Intensity Mismatch" puts a whole decode step near 1 FLOP per byte on an H100
+# with 3.35 TB/s of HBM3 and nearly 1000 dense FP16 TFLOPS.
+PAGES_CONTEXT = {"gpu": "H100 (the pages' example)", "hbm_TB_s": 3.35, "fp16_dense_TFLOPS": 1000,
+                 "decode_step_flop_per_byte": 1.0}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("decode.hip", "plan.h", "kernels.h"):
@@ -600,6 +623,8 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
         "achievable_peak": None,
+        "context": dict(PAGES_CONTEXT, attention_flop_per_byte_here=round(
+            attention_flops(wl, args.window, T) / alg, 3)),
     }
     # the other pool copies are freed before the 4 GiB streaming read; the
     # first one stays for the CPU baseline, which reads its blocks back

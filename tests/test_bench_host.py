@@ -87,3 +87,17 @@ def test_tensor_parallel_shard_needs_divisible_heads():
         workloads.shard_workload(1, 8)          # 4 KV heads
     with pytest.raises(ValueError):
         workloads.shard_workload(2, 3)
+
+
+@pytest.mark.parametrize("window,new_tokens", [(0, 1), (5, 1), (0, 3)])
+def test_attention_flops_count_every_attended_token(window, new_tokens):
+    """The reported arithmetic intensity's FLOPs: 4 D per query head and
+    attended token, counted token by token."""
+    wl = workloads.custom_workload([1, 7, 40], n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                   block_size=16, kv_dtype="bf16", io_dtype="bf16")
+    want = 0
+    for L in wl.context_lens.tolist():
+        for i in range(new_tokens):
+            visible = L - new_tokens + i + 1
+            want += 4 * 8 * 64 * (min(visible, window) if window else visible)
+    assert bench.attention_flops(wl, window, new_tokens) == want
