@@ -195,31 +195,49 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def achievable_peak(device, n_bytes: int = 4 << 30, reps: int = 10) -> dict:
-    """What a plain streaming read of one large buffer reaches on this GPU
-    (pkv_stream_read: the attention kernel's 16-byte nontemporal loads, no
-    arithmetic), timed with events over `reps` reads."""
+def achievable_peak(device, n_bytes: int = 4 << 30, reps: int = 10,
+                    step_bytes: int = 0) -> dict:
+    """What a plain streaming read reaches on this GPU (pkv_stream_read: the
+    attention kernel's 16-byte nontemporal loads, no arithmetic), timed with
+    events: one large buffer read `reps` times, and, with `step_bytes` up to
+    half of it, reads of `step_bytes` each, back to back, rotating over the
+    buffer's disjoint regions (at least two, together far larger than the
+    256 MB Infinity Cache) so that no read finds its data in a cache: the
+    step's own bytes moved at the step's own size, with the launch, ramp and
+    drain costs a step of that size meets."""
     import torch
     import paged_kv_decode_step_amd as pkv
 
     src = torch.empty(n_bytes, dtype=torch.uint8, device=device)
     sink = torch.zeros(256, dtype=torch.int32, device=device)
-    for _ in range(3):
-        pkv.stream_read(src, sink)
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        pkv.stream_read(src, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+
+    def timed(views, n):
+        for v in views:
+            pkv.stream_read(v, sink)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(n):
+            pkv.stream_read(views[k % len(views)], sink)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed([src], reps)
+    gbs = n_bytes / (ms * 1e-3) / 1e9
+    out = {"kernel": "pkv_stream_read (16-byte nontemporal loads, one pass)",
+           "bytes": n_bytes, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+           "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "at_step_bytes": None}
+    nb = step_bytes // 16 * 16
+    if nb > 0 and 2 * nb <= n_bytes:
+        views = [src[i * nb:(i + 1) * nb] for i in range(n_bytes // nb)]
+        ms_s = timed(views, max(48, 2 * len(views)))
+        gbs_s = nb / (ms_s * 1e-3) / 1e9
+        out["at_step_bytes"] = {"bytes": nb, "regions": len(views), "us": round(ms_s * 1e3, 2),
+                                "GB/s": round(gbs_s, 1), "frac_of_peak": round(gbs_s / PEAK_HBM_GBS, 4)}
     del src, sink
     torch.cuda.empty_cache()
-    gbs = n_bytes / (ms * 1e-3) / 1e9
-    return {"kernel": "pkv_stream_read (16-byte nontemporal loads, one pass)",
-            "bytes": n_bytes, "ms": round(ms, 4), "GB/s": round(gbs, 1),
-            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def cpu_baseline(wl, pool, tens, scales, budget_s: float, window: int = 0):
@@ -630,7 +648,10 @@ def main():
     # first one stays for the CPU baseline, which reads its blocks back
     for p in pools[1:]:
         p.close()
-    result["achievable_peak"] = achievable_peak(device)
+    result["achievable_peak"] = achievable_peak(device, step_bytes=alg)
+    at = result["achievable_peak"]["at_step_bytes"]
+    if at:   # the attention kernel against a plain read of the same bytes
+        result["roofline"]["frac_of_plain_read_at_step_bytes"] = round(achieved / at["GB/s"], 4)
     if args.cpu_budget > 0 and T == 1:
         result["cpu_baseline"] = cpu_baseline(wl, pools[0], t, scales, args.cpu_budget,
                                               args.window)
