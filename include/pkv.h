@@ -308,7 +308,10 @@ pkv_status kv_pool_device_errors(pkv_pool* pool, uint32_t* flags);
  *  - waves_per_cu: wavefronts per compute unit (0 = as many as are resident
  *    at once, 8 on gfx950).
  *  - min_units: fewest units the lightest wavefront is given before fewer
- *    wavefronts are used (>= 1; raised to piece_cost + 1; default 16).
+ *    wavefronts are used (>= 1; raised to piece_cost + 1; default 16); a step
+ *    too small to fill the first workgroup of every compute unit that way
+ *    goes down to a quarter of it, never below piece_cost + 1, on at most
+ *    those wavefronts (pkv_plan_host states the rule).
  *  - piece_cost: in [0, 64], or -1 (the default) for ring_tiles + 2.  A
  *    sequence start waits for the wavefront's whole ring of in-flight tile
  *    loads and then for its own query loads.
@@ -501,8 +504,13 @@ pkv_status pkv_rope_table_host(double theta, int32_t head_dim,
  * floor(U * Omega(w) / Omega(W)), and W is the largest value <= n_waves (and
  * >= 1) with U * a_min * p_min >= m * Omega(W), where m = max(min_units,
  * piece_cost + 1) and a_min * p_min is the lightest weight any of the
- * n_waves wavefronts has: every active wavefront gets at least m units.  A
- * wavefront takes the tiles whose first unit falls in its range.
+ * n_waves wavefronts has: every active wavefront gets at least m units.  If
+ * that W is below min(n_first, n_waves) (a step too small to fill the first
+ * workgroup of every compute unit), W is instead the largest value with the
+ * same inequality for m' = max(m / 4, piece_cost + 1), capped at
+ * min(n_first, n_waves): small steps are latency-bound, and more wavefronts
+ * with fewer tiles each finish sooner.  A wavefront takes the tiles whose
+ * first unit falls in its range.
  * With window >= 1 a sequence of context L costs only the tiles from its
  * window's first one, floor(max(L - window, 0) / 16), on.
  * decode_step uses n_first = the first workgroup on each compute unit (4

@@ -486,7 +486,7 @@ void decode_attn_kernel(DecodeParams p, const int32_t* __restrict__ tables,
   const int64_t U = uniform(sP[B]);
   const WaveWeights ww = weights_for(U, p.n_waves, p.weight_min_share,
                                      WaveWeights{p.weight_first, p.weight_rest, p.n_first, p.weight_odd});
-  const int64_t W = uniform((int)active_waves(U, p.n_waves, p.min_units, ww));
+  const int64_t W = uniform((int)active_waves(U, p.n_waves, p.min_units, cost, ww));
   const int wave = uniform(blockIdx.x * (kBlockThreads / 64) + wid);
 #ifdef PKV_TIMELINE
   auto record = [&](uint64_t s1, uint64_t s2, uint64_t s3, uint64_t s4, uint64_t s5, int tiles)

@@ -140,7 +140,7 @@ pkv_status pkv_plan_host(const int32_t* context_lens, int32_t batch, int32_t n_k
   const int64_t C = P[batch];
   const pkv::WaveWeights ww = pkv::weights_for(
       C, n_waves, weight_min_share, pkv::WaveWeights{weight_first, weight_rest, n_first, weight_odd});
-  const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1), ww);
+  const int64_t W = pkv::active_waves(C, n_waves, std::max(min_units, cost + 1), cost, ww);
   const int64_t n_tiles = (int64_t)P[batch] - (int64_t)hkv * cost * batch;
   for (int64_t w = 0; w < n_waves; ++w) {
     int32_t* row = splits + 4 * w;

@@ -30,7 +30,10 @@
 //  * W is the most wavefronts (at most n_waves) that would still give a
 //    wavefront of the lightest weight min_units units, and min_units > A:
 //    every window of A + 1 consecutive units holds the first unit of some
-//    tile, so every active wavefront owns at least one tile;
+//    tile, so every active wavefront owns at least one tile.  A step too
+//    small to give the first workgroup of every compute unit that much is
+//    spread over up to those wavefronts with smaller shares, still > A
+//    (active_waves);
 //  * a sequence cut between wavefronts ("split") leaves one partial softmax
 //    state per piece; a second kernel merges them.
 //
@@ -142,16 +145,40 @@ PKV_HD inline int64_t weight_index(int64_t x, const WaveWeights& k) {
                : parity_index(sf + floor_div(x - f, k.wb), k.po);
 }
 
+// Smallest share a small step's wavefronts are given (see active_waves):
+// min_units / 4, and never less than cost + 1 units, which still gives every
+// active wavefront a tile.
+PKV_HD inline int64_t small_share(int64_t min_units, int64_t cost) {
+  const int64_t q = min_units / 4;
+  return q > cost + 1 ? q : cost + 1;
+}
+
 // Active wavefronts: the most (at most n_waves, at least 1) with
-// Omega(W) <= U * w_min / min_units, w_min the lightest weight any of the
-// n_waves wavefronts has; then every active one gets at least min_units
-// units, U * weight / Omega(W) >= min_units.
+// Omega(W) <= U * w_min / m, w_min the lightest weight any of the n_waves
+// wavefronts has; then every active one gets at least m units,
+// U * weight / Omega(W) >= m.  m is min_units, except for a step so small
+// that min_units each would leave some of the first n_first wavefronts (the
+// first workgroup on each compute unit) idle.  Such a step is latency-bound:
+// each wavefront's chain of a few tiles sets its time, not the memory.  It
+// is spread further, with m = small_share(min_units, cost), over at most
+// n_first wavefronts, which run one to a SIMD.  Measured on the
+// Llama-3-8B-shaped batch with a 256-token window (665 wavefronts at 16
+// units each, 11 tiles apiece) and on 3 requests of 84-1012 tokens
+// (24 wavefronts), attention us at m = 16 / 12 / 10 / 8 / 7: 27.0 / 25.4 /
+// 28.3 / 28.0 / 25.8 (the dips where the second workgroups join) and
+// 23.4 / 20.5 / 19.3 / 16.7 / 15.8.
 PKV_HD inline int64_t active_waves(int64_t n_units, int64_t n_waves, int64_t min_units,
-                                   const WaveWeights& k) {
+                                   int64_t cost, const WaveWeights& k) {
   const int64_t age = n_waves > k.n_first ? k.wb : k.wa;
   const int64_t par = n_waves > 4 && k.po < 100 ? k.po : 100;
   int64_t W = weight_index(floor_div(n_units * age * par, min_units), k);
   if (W > n_waves) W = n_waves;
+  const int64_t cap = k.n_first < n_waves ? k.n_first : n_waves;
+  const int64_t ms = small_share(min_units, cost);
+  if (W < cap && ms < min_units) {
+    const int64_t Ws = weight_index(floor_div(n_units * age * par, ms), k);
+    W = Ws < cap ? Ws : cap;          // Ws >= W, as ms < min_units
+  }
   return W < 1 ? 1 : W;
 }
 

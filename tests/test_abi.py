@@ -110,7 +110,9 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
     w < n_first else wr) * (wo if (w // 4) is odd else 100); the most waves
     whose exact share for a wave of the lightest of all n_waves weights is
     >= max(min_units, cost + 1) units are used (found by trying every
-    count); the units are cut at floor(total * weights before w / all
+    count), unless they are fewer than min(n_first, n_waves): then the most
+    waves, up to that many, whose share is >= max(that // 4, cost + 1) units;
+    the units are cut at floor(total * weights before w / all
     weights) and each tile is owned by the wave holding its first unit.  With a
     window of W >= 1 tokens a sequence's tiles start at the one holding token
     L - W (when L > W), and are numbered from there."""
@@ -138,6 +140,10 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
         return total * lightest >= m * sum(weight[:count])
 
     we = max([c for c in range(1, n_waves + 1) if enough(c)], default=1)
+    cap = min(n_first, n_waves)
+    if we < cap and max(m // 4, cost + 1) < m:
+        m = max(m // 4, cost + 1)
+        we = max([c for c in range(1, cap + 1) if enough(c)], default=1)
     om = sum(weight[:we])
     bounds = [(total * sum(weight[:w])) // om for w in range(we + 1)]
     owner = {}
@@ -171,6 +177,13 @@ def reference_partition(lens, hkv, cap, n_waves, min_units, cost, n_first=0, wf=
     ([16, 17, 15, 32, 33], 1, 5, 1, 0, 2, 5, 3),
     ([9 * 16 - 3], 1, 2, 16, 8, 0, 1, 1),     # U = m + 1
     ([23, 10], 2, 64, 6, 5, 0, 1, 1),         # ceil(U/m) = 5 waves would leave wave 3 no tile
+    # steps too small for the first workgroups at min_units each: shares down
+    # to max(min_units // 4, cost + 1), capped at n_first (32) or not (64)
+    ([138, 1012, 84], 4, 64, 16, 6, 32, 1, 1),
+    ([138, 1012, 84], 4, 128, 16, 6, 64, 1, 1),
+    ([138, 1012, 84], 4, 128, 16, 6, 64, 100, 57),
+    ([138, 1012, 84], 4, 128, 40, 2, 64, 1, 1),
+    (list(np.random.default_rng(3).integers(1, 300, 9)), 2, 256, 24, 4, 128, 100, 65),
 ])
 @pytest.mark.parametrize("min_share", [0, 40])
 @pytest.mark.parametrize("wo", [100, 90, 37, 1])
