@@ -1,7 +1,9 @@
 """The timeline build (libpkv_timeline.so): the same kernels with
-per-wavefront phase stamps.  Its step matches the oracle like the normal
-build's, and every wavefront's record is whole and ordered; the normal
-build refuses to read a timeline."""
+per-wavefront phase stamps.  Its steps match the oracle like the normal
+build's, every wavefront's record is whole and ordered, and the tiles each
+wavefront recorded are those the host replay of the partition gives it (a
+full step, a small one spread over the first workgroups, a windowed one);
+the normal build refuses to read a timeline."""
 import json
 import os
 import subprocess
@@ -36,17 +38,24 @@ def test_timeline_build_matches_oracle_and_records_every_wavefront():
     res = subprocess.run([sys.executable, os.path.join(HERE, "timeline_child.py")],
                          capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
-    d = json.loads(res.stdout.strip().splitlines()[-1])
-    assert d["err"] <= d["tol"], d["err"]
-    rec = np.array(d["records"], dtype=np.int64)
-    assert rec.shape == (d["n_waves"], 8)
-    stamps, tiles = rec[:, :6], rec[:, 6]
-    assert (stamps[:, 0] > 0).all()                      # every wavefront recorded its entry
-    assert (np.diff(stamps, axis=1) >= 0).all()          # phases in order
-    assert tiles.sum() == d["tiles_expected"]            # every tile belongs to one wavefront
-    assert ((rec[:, 7] >> 32) & 0xF).max() < 8           # XCC ids
-    span = (stamps[:, 5].max() - stamps[:, 0].min()) / 100.0
-    assert 0.0 < span < 10_000.0                         # microseconds, one small step
+    cases = json.loads(res.stdout.strip().splitlines()[-1])
+    assert len(cases) == 3
+    for d in cases:
+        assert d["err"] <= d["tol"], d["err"]
+        rec = np.array(d["records"], dtype=np.int64)
+        assert rec.shape == (d["n_waves"], 8)
+        stamps, tiles = rec[:, :6], rec[:, 6]
+        assert (stamps[:, 0] > 0).all()                  # every wavefront recorded its entry
+        assert (np.diff(stamps, axis=1) >= 0).all()      # phases in order
+        assert tiles.sum() == d["tiles_expected"]        # every tile belongs to one wavefront
+        # the device's partition is the host replay's, wavefront by wavefront
+        assert np.array_equal(tiles, np.array(d["tiles_per_wave_expected"]))
+        assert ((rec[:, 7] >> 32) & 0xF).max() < 8       # XCC ids
+        span = (stamps[:, 5].max() - stamps[:, 0].min()) / 100.0
+        assert 0.0 < span < 10_000.0                     # microseconds, one small step
+    # the small step uses more wavefronts than min_units alone would give it
+    small = np.array(cases[1]["records"])[:, 6]
+    assert (small > 0).sum() > 24
 
 
 @pytest.mark.skipif(not os.path.exists(pkv.TIMELINE_LIB_PATH),
